@@ -1,0 +1,199 @@
+/*
+ * tara.h - C ABI of the MI355X (gfx950) TARA attention library (libtara.so).
+ *
+ * TARA ("TARA: Native Temporal Alignment for MiniMax H3 References", section
+ * "The temporal rule") is scaled-dot-product attention over one packed token
+ * sequence (output video, selected motion-guide video, reference pictures,
+ * text, ...) in which only logits from output-video (target) queries to guide
+ * keys are lowered by a temporal penalty
+ *
+ *     dt      = |t_query - t_key|                                    (seconds)
+ *     penalty = min(strength * (max(dt - window, 0) / falloff)^2, cap)
+ *     logit   = (Q . K) * softmax_scale - penalty
+ *
+ * and, with reference binding on ("BFS H3 Reference Attention Binding
+ * (Experimental)", section "The exact rule"), logits from target queries with
+ * mask weight m to keys of Picture i gain m * ln(gain_i). Every other logit is
+ * plain (Q . K) * softmax_scale. One non-causal softmax runs over all keys of
+ * the sequence. The library returns O and the natural-log log-sum-exp (LSE) of
+ * each query row's final logits.
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are HIP device memory of the current device; host
+ *    pointers are marked "host". The caller owns every buffer; the library never
+ *    allocates, frees or retains device memory between calls.
+ *  - All work is enqueued asynchronously on `stream` (NULL = default stream);
+ *    inputs and workspace must stay valid until the stream has passed the call.
+ *  - Return value: TARA_OK (0) or a negative tara_status_t. Argument errors are
+ *    detected on the host before any device work is enqueued, so a failing call
+ *    leaves outputs untouched. tara_last_error() gives the detail (per thread).
+ *  - Thread safety: calls from several host threads are safe; concurrent calls
+ *    on one stream serialise in stream order.
+ */
+#ifndef TARA_H_
+#define TARA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* tara_stream_t; /* a hipStream_t */
+
+/* Segment codes of seg_type[]: which part of the packed sequence a token is.
+ * TARGET = output video (the only biased queries); GUIDE = the motion video
+ * selected by motion_video_index (the only temporally penalised keys; "Wiring
+ * it" section); PICTURE = a native reference picture (binding keys);
+ * OTHER = text, reference audio, other videos: plain attention both ways. */
+enum {
+  TARA_SEG_TARGET = 0,
+  TARA_SEG_GUIDE = 1,
+  TARA_SEG_PICTURE = 2,
+  TARA_SEG_OTHER = 3
+};
+
+typedef enum { TARA_BF16 = 0, TARA_FP32 = 1 } tara_dtype_t;
+
+/* FUSED: one streaming pass over all keys.
+ * PARTITIONED: the keys are split into num_partitions contiguous ranges, each
+ * range is attended on its own with its own LSE, and the ranges are merged
+ * exactly by log-sum-exp (the LSE-merging evaluation of the "Three backends"
+ * section). Both modes return the same O and LSE up to rounding. */
+typedef enum { TARA_MODE_FUSED = 0, TARA_MODE_PARTITIONED = 1 } tara_mode_t;
+
+typedef enum {
+  TARA_OK = 0,
+  TARA_ERR_NULL_POINTER = -1,       /* a required pointer is NULL */
+  TARA_ERR_BAD_SHAPE = -2,          /* B, H or N negative or too large */
+  TARA_ERR_UNSUPPORTED_DTYPE = -3,  /* dtype not TARA_BF16 / TARA_FP32 */
+  TARA_ERR_UNSUPPORTED_HEAD_DIM = -4, /* D not 64 or 128 */
+  TARA_ERR_BAD_STRIDE = -5,         /* base or stride not 16-byte aligned, or negative */
+  TARA_ERR_BAD_PARAM = -6,          /* a control out of range (see tara_params_t) */
+  TARA_ERR_WORKSPACE = -7,          /* workspace NULL or smaller than tara_workspace_bytes() */
+  TARA_ERR_BAD_METADATA = -8,       /* only with TARA_VALIDATE=1: metadata out of range */
+  TARA_ERR_HIP = -9                 /* a HIP runtime call failed (message in tara_last_error) */
+} tara_status_t;
+
+#define TARA_MAX_PICTURES 16
+#define TARA_MAX_PARTITIONS 64
+
+/* Controls of one call. Start from tara_params_default().
+ *  window, falloff, strength, cap: the four TARA controls ("The temporal rule";
+ *    defaults 0.20 s, 0.25 s, 2.0, 6.0). Valid: finite, window >= 0,
+ *    falloff > 0, strength >= 0, cap >= 0. strength == 0 or cap == 0 removes
+ *    the temporal bias (plain attention on those edges).
+ *  binding_enabled, num_pictures, picture_gain: reference binding ("Inputs
+ *    you'll set": picture_index chooses the Picture whose gain is
+ *    reference_strength, the other pictures get other_reference_strength;
+ *    1 is neutral). Here the gain is given per 0-based picture id,
+ *    0 <= id < num_pictures <= TARA_MAX_PICTURES; every gain must be finite
+ *    and > 0. binding_enabled == 0 ignores picture_id, mask_weight and gains.
+ *  softmax_scale: multiplies Q . K only; 0 selects 1/sqrt(D).
+ *  mode, num_partitions, partition_bounds: see tara_mode_t. partition_bounds
+ *    is a host array of num_partitions + 1 non-decreasing key offsets from 0 to
+ *    N (empty ranges allowed), or NULL for num_partitions near-equal ranges;
+ *    1 <= num_partitions <= TARA_MAX_PARTITIONS. */
+typedef struct {
+  float window;
+  float falloff;
+  float strength;
+  float cap;
+  int binding_enabled;
+  int num_pictures;
+  float picture_gain[TARA_MAX_PICTURES];
+  float softmax_scale;
+  int mode;
+  int num_partitions;
+  const int32_t* partition_bounds;
+} tara_params_t;
+
+/* Fills *p with the defaults: window 0.20, falloff 0.25, strength 2.0,
+ * cap 6.0, binding off (all gains 1), scale 1/sqrt(D), fused mode. */
+void tara_params_default(tara_params_t* p);
+
+/* Device workspace tara_attn_fwd needs for this call shape (bytes, a multiple
+ * of 256). It holds per-token encodings of the metadata, per-key-tile
+ * summaries, V laid out key-contiguous per (batch, head, dim) for the bf16
+ * path, and per-partition O/LSE in partitioned mode. Returns 0 for an empty
+ * call (B, H or N == 0) and (size_t)-1 for arguments tara_attn_fwd would reject
+ * (p == NULL, bad dtype or head dim, bad partition count). */
+size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
+                            const tara_params_t* p);
+
+/* TARA-biased attention forward: O = softmax(logits) V and LSE per query row.
+ *
+ *  q, k, v  device, dtype elements, logical shape [B][H][N][D], element
+ *           (b,h,n,d) at base + b*str[0] + h*str[1] + n*str[2] + d (d contiguous).
+ *           Base addresses 16-byte aligned; every stride a multiple of
+ *           16 bytes / sizeof(element) and >= 0.
+ *  o        device, same dtype and layout rules (strides o_str); fully written.
+ *  lse      device fp32 [B][H][N] contiguous, natural log; fully written.
+ *  dtype    TARA_BF16 (bf16 in and out, fp32 accumulation) or TARA_FP32.
+ *  D        64 or 128.
+ *  seg_type device uint8 [B][N], TARA_SEG_* codes.
+ *  token_time device fp32 [B][N], seconds on the aligned output clock; read
+ *           only for TARGET and GUIDE tokens (others may hold anything).
+ *  picture_id device int16 [B][N], 0-based picture id of PICTURE tokens; read
+ *           only when binding is active; may be NULL when it is not.
+ *  mask_weight device fp32 [B][N] mask weight m of TARGET queries, or NULL for
+ *           m = 1 everywhere ("no mask means the whole output video").
+ *  p        host, the controls (see tara_params_t).
+ *  workspace device, >= tara_workspace_bytes(...) bytes, 256-byte aligned;
+ *           contents on entry are ignored, on exit unspecified.
+ *  stream   HIP stream the work is enqueued on.
+ *
+ * Metadata out of range (seg_type > 3, picture id outside [0, num_pictures),
+ * non-finite time on a TARGET/GUIDE token) is not an error by default: such a
+ * token gets no bias term, never an out-of-bounds read. With the environment
+ * variable TARA_VALIDATE=1 the metadata is copied to the host and checked
+ * first (synchronously), returning TARA_ERR_BAD_METADATA.
+ * B, H or N == 0 is a valid empty call and enqueues nothing. */
+int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  tara_dtype_t dtype, int B, int H, int N, int D,
+                  const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
+                  const int64_t o_str[3],
+                  const uint8_t* seg_type, const float* token_time,
+                  const int16_t* picture_id, const float* mask_weight,
+                  const tara_params_t* p, void* workspace, size_t workspace_bytes,
+                  tara_stream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* tara_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none). The pointer
+ * stays valid until this thread's next tara_* call. */
+const char* tara_last_error(void);
+
+/* What the last successful tara_attn_fwd on this thread ran. */
+typedef struct {
+  int mode;              /* tara_mode_t */
+  int dtype;             /* tara_dtype_t */
+  int bias_active;       /* strength > 0 and cap > 0 */
+  int binding_active;    /* binding_enabled and some gain != 1 */
+  int num_partitions;    /* 1 in fused mode */
+  int block_q;           /* query rows per workgroup of the attention kernel */
+  int block_k;           /* keys per tile */
+  int grid;              /* workgroups of the attention kernel (all partitions) */
+  int launches;          /* kernels enqueued by the call */
+} tara_run_info_t;
+
+/* Copies the run info of this thread's last successful call; TARA_ERR_NULL_POINTER
+ * if info is NULL. */
+int tara_get_last_run_info(tara_run_info_t* info);
+
+/* Per-launch timing of the attention kernel, for measurement. With timing on,
+ * every tara_attn_fwd records a HIP event pair on its stream around the
+ * attention kernel (the partition merge is not included). tara_timing_read
+ * waits for the recorded pairs, writes up to `max` durations in milliseconds
+ * to ms_out (host), sets *count to how many were written, and forgets all
+ * recorded pairs. Global to the process (not per thread). */
+int tara_timing_enable(int on);
+int tara_timing_read(float* ms_out, int max, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TARA_H_ */

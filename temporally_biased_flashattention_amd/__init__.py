@@ -1,0 +1,254 @@
+"""Python binding of libtara.so, the MI355X (gfx950) TARA attention library.
+
+Thin ctypes marshalling over the C ABI in include/tara.h: the functions keep
+the C names (tara_attn_fwd, tara_workspace_bytes, ...), take torch tensors for
+device buffers and pass their pointers, strides and the current HIP stream.
+Every step of the computation runs in the library's kernels; there is no
+fallback path. If libtara.so is missing, calls raise TaraLibraryMissing.
+
+What is computed ("TARA: Native Temporal Alignment for MiniMax H3
+References", section "The temporal rule"; "BFS H3 Reference Attention Binding
+(Experimental)", section "The exact rule"): softmax attention over a packed
+sequence where target-query x guide-key logits lose
+min(strength*(max(|t_q - t_k| - window, 0)/falloff)^2, cap) and, with binding,
+target-query x picture-key logits gain m*ln(gain).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "TARA_SEG_TARGET", "TARA_SEG_GUIDE", "TARA_SEG_PICTURE", "TARA_SEG_OTHER",
+    "TARA_BF16", "TARA_FP32", "TARA_MODE_FUSED", "TARA_MODE_PARTITIONED",
+    "TaraError", "TaraLibraryMissing", "TaraParams", "TaraRunInfo",
+    "tara_params_default", "make_params", "tara_workspace_bytes", "tara_attn_fwd",
+    "tara_status_string", "tara_last_error", "tara_get_last_run_info",
+    "tara_timing_enable", "tara_timing_read", "attn_fwd", "library_path", "load_library",
+    "EXPORTED_SYMBOLS",
+]
+
+TARA_SEG_TARGET, TARA_SEG_GUIDE, TARA_SEG_PICTURE, TARA_SEG_OTHER = 0, 1, 2, 3
+TARA_BF16, TARA_FP32 = 0, 1
+TARA_MODE_FUSED, TARA_MODE_PARTITIONED = 0, 1
+TARA_MAX_PICTURES = 16
+TARA_MAX_PARTITIONS = 64
+
+EXPORTED_SYMBOLS = (
+    "tara_params_default", "tara_workspace_bytes", "tara_attn_fwd", "tara_status_string",
+    "tara_last_error", "tara_get_last_run_info", "tara_timing_enable", "tara_timing_read",
+)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.environ.get("TARA_LIBRARY", os.path.join(_PKG, "libtara.so"))
+
+
+class TaraLibraryMissing(RuntimeError):
+    pass
+
+
+class TaraError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"tara error {status} ({tara_status_string(status)}): {detail}")
+
+
+class TaraParams(ctypes.Structure):
+    _fields_ = [
+        ("window", ctypes.c_float),
+        ("falloff", ctypes.c_float),
+        ("strength", ctypes.c_float),
+        ("cap", ctypes.c_float),
+        ("binding_enabled", ctypes.c_int),
+        ("num_pictures", ctypes.c_int),
+        ("picture_gain", ctypes.c_float * TARA_MAX_PICTURES),
+        ("softmax_scale", ctypes.c_float),
+        ("mode", ctypes.c_int),
+        ("num_partitions", ctypes.c_int),
+        ("partition_bounds", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class TaraRunInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "mode", "dtype", "bias_active", "binding_active", "num_partitions",
+        "block_q", "block_k", "grid", "launches")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load_library():
+    """Loads libtara.so once and declares the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise TaraLibraryMissing(
+            f"{path} is not built; run `python -m temporally_biased_flashattention_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64_3 = ctypes.POINTER(ctypes.c_int64)
+    lib.tara_params_default.argtypes = [ctypes.POINTER(TaraParams)]
+    lib.tara_params_default.restype = None
+    lib.tara_workspace_bytes.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(TaraParams)]
+    lib.tara_workspace_bytes.restype = ctypes.c_size_t
+    lib.tara_attn_fwd.argtypes = ([P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, I64_3, I64_3, I64_3, I64_3, P, P, P, P,
+                                   ctypes.POINTER(TaraParams), P, ctypes.c_size_t, P])
+    lib.tara_attn_fwd.restype = ctypes.c_int
+    lib.tara_status_string.argtypes = [ctypes.c_int]
+    lib.tara_status_string.restype = ctypes.c_char_p
+    lib.tara_last_error.argtypes = []
+    lib.tara_last_error.restype = ctypes.c_char_p
+    lib.tara_get_last_run_info.argtypes = [ctypes.POINTER(TaraRunInfo)]
+    lib.tara_get_last_run_info.restype = ctypes.c_int
+    lib.tara_timing_enable.argtypes = [ctypes.c_int]
+    lib.tara_timing_enable.restype = ctypes.c_int
+    lib.tara_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.tara_timing_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- params
+def tara_params_default() -> TaraParams:
+    p = TaraParams()
+    load_library().tara_params_default(ctypes.byref(p))
+    return p
+
+
+def make_params(window: float = 0.20, falloff: float = 0.25, strength: float = 2.0, cap: float = 6.0,
+                binding: bool = False, gains: Sequence[float] = (), softmax_scale: float = 0.0,
+                mode: str = "fused", partitions: int = 1,
+                bounds: Optional[Sequence[int]] = None) -> TaraParams:
+    """Builds tara_params_t. gains[i] is the gain of 0-based picture id i."""
+    p = tara_params_default()
+    p.window, p.falloff, p.strength, p.cap = window, falloff, strength, cap
+    p.binding_enabled = int(bool(binding))
+    p.num_pictures = len(gains)
+    if len(gains) > TARA_MAX_PICTURES:
+        raise ValueError("at most 16 pictures")
+    for i, g in enumerate(gains):
+        p.picture_gain[i] = g
+    p.softmax_scale = softmax_scale
+    p.mode = {"fused": TARA_MODE_FUSED, "partitioned": TARA_MODE_PARTITIONED}[mode]
+    p.num_partitions = int(partitions)
+    if bounds is not None:
+        arr = (ctypes.c_int32 * len(bounds))(*[int(x) for x in bounds])
+        p._bounds_keepalive = arr  # noqa: SLF001 (keeps the host array alive)
+        p.partition_bounds = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return p
+
+
+# ----------------------------------------------------------------- calls
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TARA_BF16
+    if t.dtype == torch.float32:
+        return TARA_FP32
+    return 99  # rejected by the library as TARA_ERR_UNSUPPORTED_DTYPE
+
+
+def _strides(t):
+    if t.dim() != 4:
+        raise ValueError("q, k, v and o must be 4-D [B, H, N, D] tensors (views allowed)")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int):
+    if status != 0:
+        raise TaraError(status, tara_last_error())
+
+
+def tara_workspace_bytes(dtype: int, B: int, H: int, N: int, D: int, params: TaraParams) -> int:
+    n = load_library().tara_workspace_bytes(dtype, B, H, N, D, ctypes.byref(params))
+    if n == ctypes.c_size_t(-1).value:
+        raise TaraError(-6, "tara_workspace_bytes rejected the arguments")
+    return int(n)
+
+
+def tara_attn_fwd(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight,
+                  params: TaraParams, workspace, stream=None) -> None:
+    """Calls tara_attn_fwd on torch device tensors.
+
+    q, k, v, o: [B, H, N, D] (any strides with a contiguous last dim);
+    lse: fp32 [B, H, N] contiguous; seg_type uint8 [B, N]; token_time fp32
+    [B, N]; picture_id int16 [B, N] or None; mask_weight fp32 [B, N] or None;
+    workspace: a byte tensor of at least tara_workspace_bytes(...) bytes.
+    stream: a torch.cuda.Stream (default: the current stream).
+    """
+    import torch
+    lib = load_library()
+    B, H, N, D = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.tara_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), B, H, N, D,
+        _strides(q), _strides(k), _strides(v), _strides(o),
+        _ptr(seg_type), _ptr(token_time), _ptr(picture_id), _ptr(mask_weight),
+        ctypes.byref(params), _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def tara_status_string(status: int) -> str:
+    return load_library().tara_status_string(status).decode()
+
+
+def tara_last_error() -> str:
+    return load_library().tara_last_error().decode()
+
+
+def tara_get_last_run_info() -> dict:
+    info = TaraRunInfo()
+    _check(load_library().tara_get_last_run_info(ctypes.byref(info)))
+    return info.as_dict()
+
+
+def tara_timing_enable(on: bool) -> None:
+    _check(load_library().tara_timing_enable(int(bool(on))))
+
+
+def tara_timing_read(max_count: int = 4096):
+    buf = (ctypes.c_float * max(max_count, 1))()
+    n = ctypes.c_int(0)
+    _check(load_library().tara_timing_read(buf, max_count, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]
+
+
+def attn_fwd(q, k, v, seg_type, token_time, picture_id=None, mask_weight=None,
+             params: Optional[TaraParams] = None, out=None, lse=None, workspace=None):
+    """Allocates O, LSE and the workspace with torch, then calls tara_attn_fwd.
+
+    Returns (O, LSE): O like q (contiguous [B, H, N, D]), LSE fp32 [B, H, N].
+    """
+    import torch
+    if params is None:
+        params = tara_params_default()
+    B, H, N, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = tara_workspace_bytes(_dtype_code(q), B, H, N, D, params)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    tara_attn_fwd(q, k, v, out, lse, seg_type, token_time, picture_id, mask_weight, params, workspace)
+    return out, lse

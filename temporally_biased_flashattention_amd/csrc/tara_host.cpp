@@ -1,0 +1,404 @@
+// Host side of the TARA attention C ABI (include/tara.h): argument checks,
+// derived constants, workspace carving and kernel dispatch. No device memory
+// is allocated here; every launch goes to the caller's stream.
+#include "tara.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "tara_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local tara_run_info_t g_info;
+thread_local bool g_info_valid = false;
+
+int fail(int status, const std::string& msg) {
+  g_err = msg;
+  return status;
+}
+
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t tq, mq, tk, kb, ksum, vt, opart, lsepart, total;
+};
+
+int npad_of(int N) { return (N + tara::kBlockK - 1) / tara::kBlockK * tara::kBlockK; }
+
+int num_parts(const tara_params_t* p) { return p->mode == TARA_MODE_PARTITIONED ? p->num_partitions : 1; }
+
+// Workspace regions, each 256-byte aligned: per-token encodings, key-tile
+// summaries, V^T (bf16 path), and per-partition O/LSE (partitioned mode).
+WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
+  WsLayout L{};
+  const size_t npad = (size_t)npad_of(N), nkt = npad / tara::kBlockK;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.tq = take((size_t)B * N * 4);
+  L.mq = take((size_t)B * N * 4);
+  L.tk = take((size_t)B * npad * 4);
+  L.kb = take((size_t)B * npad * 4);
+  L.ksum = take((size_t)B * nkt * sizeof(tara::KeyTileSummary));
+  L.vt = dtype == TARA_BF16 ? take((size_t)B * H * D * npad * 2) : 0;
+  if (p->mode == TARA_MODE_PARTITIONED) {
+    const size_t parts = (size_t)p->num_partitions;
+    L.opart = take(parts * B * H * N * D * 4);
+    L.lsepart = take(parts * B * H * N * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+int check_params(const tara_params_t* p, int N) {
+  if (!finite(p->window) || !finite(p->falloff) || !finite(p->strength) || !finite(p->cap))
+    return fail(TARA_ERR_BAD_PARAM, "window, falloff, strength and cap must be finite");
+  if (p->window < 0.0f) return fail(TARA_ERR_BAD_PARAM, "window must be >= 0");
+  if (!(p->falloff > 0.0f)) return fail(TARA_ERR_BAD_PARAM, "falloff must be > 0");
+  if (p->strength < 0.0f) return fail(TARA_ERR_BAD_PARAM, "strength must be >= 0");
+  if (p->cap < 0.0f) return fail(TARA_ERR_BAD_PARAM, "cap must be >= 0");
+  if (!finite(p->softmax_scale) || p->softmax_scale < 0.0f)
+    return fail(TARA_ERR_BAD_PARAM, "softmax_scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  if (p->binding_enabled) {
+    if (p->num_pictures < 0 || p->num_pictures > TARA_MAX_PICTURES)
+      return fail(TARA_ERR_BAD_PARAM, "num_pictures must be in [0, 16]");
+    for (int i = 0; i < p->num_pictures; ++i)
+      if (!finite(p->picture_gain[i]) || !(p->picture_gain[i] > 0.0f))
+        return fail(TARA_ERR_BAD_PARAM, "picture gains must be finite and > 0 (the rule adds m*ln(gain))");
+  }
+  if (p->mode != TARA_MODE_FUSED && p->mode != TARA_MODE_PARTITIONED)
+    return fail(TARA_ERR_BAD_PARAM, "mode must be TARA_MODE_FUSED or TARA_MODE_PARTITIONED");
+  if (p->mode == TARA_MODE_PARTITIONED) {
+    if (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS)
+      return fail(TARA_ERR_BAD_PARAM, "num_partitions must be in [1, 64]");
+    if (p->partition_bounds) {
+      const int32_t* pb = p->partition_bounds;
+      if (pb[0] != 0 || pb[p->num_partitions] != N)
+        return fail(TARA_ERR_BAD_PARAM, "partition_bounds must start at 0 and end at N");
+      for (int i = 0; i < p->num_partitions; ++i)
+        if (pb[i + 1] < pb[i]) return fail(TARA_ERR_BAD_PARAM, "partition_bounds must be non-decreasing");
+    }
+  }
+  return TARA_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+int check_strides(const char* name, const void* base, const int64_t* s, int esize) {
+  if (!s) return fail(TARA_ERR_NULL_POINTER, std::string(name) + " strides are NULL");
+  if (!aligned16(base)) return fail(TARA_ERR_BAD_STRIDE, std::string(name) + " base is not 16-byte aligned");
+  const int64_t q = 16 / esize;
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || s[i] % q != 0)
+      return fail(TARA_ERR_BAD_STRIDE, std::string(name) + " strides must be >= 0 and multiples of " +
+                                           std::to_string(q) + " elements");
+  return TARA_OK;
+}
+
+// Optional synchronous metadata check (TARA_VALIDATE=1).
+int validate_metadata(int B, int N, const uint8_t* seg, const float* time, const int16_t* pic,
+                      const float* mask, const tara_params_t* p, hipStream_t stream) {
+  const size_t n = (size_t)B * N;
+  std::vector<uint8_t> hs(n);
+  std::vector<float> ht(n), hm;
+  std::vector<int16_t> hp;
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(hs.data(), seg, n, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(ht.data(), time, n * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(TARA_ERR_HIP, "TARA_VALIDATE: copying metadata to the host failed");
+  const bool bind = p->binding_enabled != 0;
+  if (bind && pic) {
+    hp.resize(n);
+    if (hipMemcpy(hp.data(), pic, n * 2, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(TARA_ERR_HIP, "TARA_VALIDATE: copying picture ids failed");
+  }
+  if (bind && mask) {
+    hm.resize(n);
+    if (hipMemcpy(hm.data(), mask, n * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(TARA_ERR_HIP, "TARA_VALIDATE: copying the mask failed");
+  }
+  for (size_t i = 0; i < n; ++i) {
+    if (hs[i] > 3) return fail(TARA_ERR_BAD_METADATA, "seg_type[" + std::to_string(i) + "] > 3");
+    if ((hs[i] == TARA_SEG_TARGET || hs[i] == TARA_SEG_GUIDE) && !std::isfinite(ht[i]))
+      return fail(TARA_ERR_BAD_METADATA, "token_time[" + std::to_string(i) + "] of a video token is not finite");
+    if (bind && hs[i] == TARA_SEG_PICTURE && !hp.empty() && (hp[i] < 0 || hp[i] >= p->num_pictures))
+      return fail(TARA_ERR_BAD_METADATA, "picture_id[" + std::to_string(i) + "] outside [0, num_pictures)");
+    if (bind && hs[i] == TARA_SEG_TARGET && !hm.empty() && !std::isfinite(hm[i]))
+      return fail(TARA_ERR_BAD_METADATA, "mask_weight[" + std::to_string(i) + "] is not finite");
+  }
+  return TARA_OK;
+}
+
+// Event timing of the attention kernel.
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
+
+}  // namespace
+
+extern "C" {
+
+void tara_params_default(tara_params_t* p) {
+  if (!p) return;
+  std::memset(p, 0, sizeof(*p));
+  p->window = 0.20f;
+  p->falloff = 0.25f;
+  p->strength = 2.0f;
+  p->cap = 6.0f;
+  p->binding_enabled = 0;
+  p->num_pictures = 0;
+  for (int i = 0; i < TARA_MAX_PICTURES; ++i) p->picture_gain[i] = 1.0f;
+  p->softmax_scale = 0.0f;
+  p->mode = TARA_MODE_FUSED;
+  p->num_partitions = 1;
+  p->partition_bounds = nullptr;
+}
+
+size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
+  if (!p || (dtype != TARA_BF16 && dtype != TARA_FP32) || (D != 64 && D != 128)) return (size_t)-1;
+  if (B < 0 || H < 0 || N < 0) return (size_t)-1;
+  if (p->mode == TARA_MODE_PARTITIONED && (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS))
+    return (size_t)-1;
+  if (B == 0 || H == 0 || N == 0) return 0;
+  return ws_layout_for(dtype, B, H, N, D, p).total;
+}
+
+const char* tara_status_string(int status) {
+  switch (status) {
+    case TARA_OK: return "ok";
+    case TARA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case TARA_ERR_BAD_SHAPE: return "bad shape (B, H or N)";
+    case TARA_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case TARA_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dim (64 or 128)";
+    case TARA_ERR_BAD_STRIDE: return "bad stride or alignment";
+    case TARA_ERR_BAD_PARAM: return "bad parameter";
+    case TARA_ERR_WORKSPACE: return "workspace missing or too small";
+    case TARA_ERR_BAD_METADATA: return "metadata out of range";
+    case TARA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* tara_last_error(void) { return g_err.c_str(); }
+
+int tara_get_last_run_info(tara_run_info_t* info) {
+  if (!info) return fail(TARA_ERR_NULL_POINTER, "info is NULL");
+  if (!g_info_valid) std::memset(info, 0, sizeof(*info));
+  else *info = g_info;
+  return TARA_OK;
+}
+
+int tara_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+  return TARA_OK;
+}
+
+int tara_timing_read(float* ms_out, int max, int* count) {
+  if (!count || (max > 0 && !ms_out)) return fail(TARA_ERR_NULL_POINTER, "ms_out/count is NULL");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  int n = 0;
+  int status = TARA_OK;
+  for (auto& ev : g_events) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(ev.second) != hipSuccess || hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess)
+      status = fail(TARA_ERR_HIP, "hipEventElapsedTime failed");
+    else if (n < max)
+      ms_out[n++] = ms;
+    (void)hipEventDestroy(ev.first);
+    (void)hipEventDestroy(ev.second);
+  }
+  g_events.clear();
+  *count = n;
+  return status;
+}
+
+int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, tara_dtype_t dtype,
+                  int B, int H, int N, int D, const int64_t q_str[3], const int64_t k_str[3],
+                  const int64_t v_str[3], const int64_t o_str[3], const uint8_t* seg_type,
+                  const float* token_time, const int16_t* picture_id, const float* mask_weight,
+                  const tara_params_t* p, void* workspace, size_t workspace_bytes, tara_stream_t stream_) {
+  g_err.clear();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  if (!p) return fail(TARA_ERR_NULL_POINTER, "params are NULL");
+  if (dtype != TARA_BF16 && dtype != TARA_FP32) return fail(TARA_ERR_UNSUPPORTED_DTYPE, "dtype must be TARA_BF16 or TARA_FP32");
+  if (D != 64 && D != 128) return fail(TARA_ERR_UNSUPPORTED_HEAD_DIM, "head dim must be 64 or 128");
+  if (B < 0 || H < 0 || N < 0) return fail(TARA_ERR_BAD_SHAPE, "B, H and N must be >= 0");
+  if ((int64_t)B * H > 65535) return fail(TARA_ERR_BAD_SHAPE, "B * H must be <= 65535");
+  if (N > (1 << 30)) return fail(TARA_ERR_BAD_SHAPE, "N must be <= 2^30");
+  if (int st = check_params(p, N)) return st;
+  if (B == 0 || H == 0 || N == 0) {
+    g_info = tara_run_info_t{p->mode, (int)dtype, 0, 0, num_parts(p), 0, tara::kBlockK, 0, 0};
+    g_info_valid = true;
+    return TARA_OK;
+  }
+  if (!q || !k || !v || !o || !lse) return fail(TARA_ERR_NULL_POINTER, "q, k, v, o and lse must be non-NULL");
+  if (!seg_type || !token_time) return fail(TARA_ERR_NULL_POINTER, "seg_type and token_time must be non-NULL");
+  const int esize = dtype == TARA_BF16 ? 2 : 4;
+  if (int st = check_strides("q", q, q_str, esize)) return st;
+  if (int st = check_strides("k", k, k_str, esize)) return st;
+  if (int st = check_strides("v", v, v_str, esize)) return st;
+  if (int st = check_strides("o", o, o_str, esize)) return st;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3) != 0) return fail(TARA_ERR_BAD_STRIDE, "lse is not 4-byte aligned");
+
+  // derived constants, in double then rounded once to fp32
+  const double log2e = 1.4426950408889634;
+  const double scale = p->softmax_scale > 0.0f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)D);
+  const bool bias_active = p->strength > 0.0f && p->cap > 0.0f;
+  bool binding_active = false;
+  if (p->binding_enabled)
+    for (int i = 0; i < p->num_pictures; ++i) binding_active |= p->picture_gain[i] != 1.0f;
+  if (binding_active && !picture_id)
+    return fail(TARA_ERR_NULL_POINTER, "picture_id must be non-NULL when binding is active");
+
+  const int parts = num_parts(p);
+  const WsLayout L = ws_layout_for(dtype, B, H, N, D, p);
+  if (!workspace) return fail(TARA_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return fail(TARA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(TARA_ERR_WORKSPACE, "workspace needs " + std::to_string(L.total) + " bytes, got " +
+                                        std::to_string(workspace_bytes));
+  if (env_flag("TARA_VALIDATE"))
+    if (int st = validate_metadata(B, N, seg_type, token_time, picture_id, mask_weight, p, stream)) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  const int npad = npad_of(N), nkt = npad / tara::kBlockK;
+
+  tara::MetaArgs ma{};
+  ma.seg = seg_type;
+  ma.time = token_time;
+  ma.pic = picture_id;
+  ma.mask = mask_weight;
+  ma.B = B;
+  ma.N = N;
+  ma.npad = npad;
+  ma.nkt = nkt;
+  ma.bias_active = bias_active;
+  ma.binding_active = binding_active;
+  ma.num_pictures = p->binding_enabled ? p->num_pictures : 0;
+  for (int i = 0; i < tara::kMaxPictures; ++i)
+    ma.lg2gain[i] = (binding_active && i < p->num_pictures) ? (float)std::log2((double)p->picture_gain[i]) : 0.0f;
+  ma.tq = reinterpret_cast<float*>(ws + L.tq);
+  ma.mq = reinterpret_cast<float*>(ws + L.mq);
+  ma.tk = reinterpret_cast<float*>(ws + L.tk);
+  ma.kb = reinterpret_cast<float*>(ws + L.kb);
+  ma.ksum = reinterpret_cast<tara::KeyTileSummary*>(ws + L.ksum);
+
+  tara::AttnArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.vt = dtype == TARA_BF16 ? reinterpret_cast<const __bf16*>(ws + L.vt) : nullptr;
+  aa.q_sb = q_str[0]; aa.q_sh = q_str[1]; aa.q_sn = q_str[2];
+  aa.k_sb = k_str[0]; aa.k_sh = k_str[1]; aa.k_sn = k_str[2];
+  aa.v_sb = v_str[0]; aa.v_sh = v_str[1]; aa.v_sn = v_str[2];
+  aa.o_sb = o_str[0]; aa.o_sh = o_str[1]; aa.o_sn = o_str[2];
+  aa.o = o;
+  aa.lse = lse;
+  aa.opart = p->mode == TARA_MODE_PARTITIONED ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
+  aa.lsepart = p->mode == TARA_MODE_PARTITIONED ? reinterpret_cast<float*>(ws + L.lsepart) : nullptr;
+  aa.B = B;
+  aa.H = H;
+  aa.N = N;
+  aa.npad = npad;
+  aa.nkt = nkt;
+  aa.tq = ma.tq;
+  aa.mq = ma.mq;
+  aa.tk = ma.tk;
+  aa.kb = ma.kb;
+  aa.ksum = ma.ksum;
+  aa.c = (float)(scale * log2e);
+  const double sigma = bias_active ? std::sqrt((double)p->strength * log2e) / (double)p->falloff : 0.0;
+  aa.sigma = (float)sigma;
+  aa.w = (float)((double)p->window * sigma);
+  aa.cap2 = bias_active ? (float)((double)p->cap * log2e) : 0.0f;
+  aa.window = p->window;
+  aa.dsat = bias_active ? (float)((double)p->window + (double)p->falloff * std::sqrt((double)p->cap / (double)p->strength))
+                        : INFINITY;
+  aa.nparts = parts;
+  if (p->mode == TARA_MODE_PARTITIONED && p->partition_bounds) {
+    for (int i = 0; i <= parts; ++i) aa.kr[i] = p->partition_bounds[i];
+  } else {
+    for (int i = 0; i <= parts; ++i) aa.kr[i] = (int)((int64_t)N * i / parts);
+  }
+  const bool partitioned = p->mode == TARA_MODE_PARTITIONED;
+  int launches = 0;
+  hipError_t e = tara::launch_meta(ma, stream);
+  ++launches;
+  if (e == hipSuccess && dtype == TARA_BF16) {
+    e = tara::launch_vtranspose(static_cast<const __bf16*>(v), v_str[0], v_str[1], v_str[2],
+                                const_cast<__bf16*>(aa.vt), B, H, N, npad, D, stream);
+    ++launches;
+  }
+  if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
+
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timing) {
+      if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
+        return fail(TARA_ERR_HIP, "hipEventCreate failed");
+      (void)hipEventRecord(ev0, stream);
+    }
+  }
+  int grid = 0, block_q = 0;
+  if (dtype == TARA_BF16) {
+    aa.nqb = (N + tara::attn_bf16_block_q(D) - 1) / tara::attn_bf16_block_q(D);
+    block_q = tara::attn_bf16_block_q(D);
+    grid = tara::attn_bf16_grid(aa) * (partitioned ? parts : 1);
+    e = tara::launch_attn_bf16(aa, D, partitioned, stream);
+  } else {
+    block_q = tara::attn_f32_block_q(D);
+    aa.nqb = (N + block_q - 1) / block_q;
+    grid = aa.nqb * B * H * (partitioned ? parts : 1);
+    e = tara::launch_attn_f32(aa, D, partitioned, stream);
+  }
+  ++launches;
+  if (ev1) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    (void)hipEventRecord(ev1, stream);
+    g_events.emplace_back(ev0, ev1);
+  }
+  if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
+  if (partitioned) {
+    tara::MergeArgs mg{};
+    mg.opart = aa.opart;
+    mg.lsepart = aa.lsepart;
+    mg.o = o;
+    mg.lse = lse;
+    mg.o_sb = o_str[0]; mg.o_sh = o_str[1]; mg.o_sn = o_str[2];
+    mg.B = B; mg.H = H; mg.N = N; mg.D = D; mg.nparts = parts;
+    e = tara::launch_merge(mg, dtype == TARA_BF16, stream);
+    ++launches;
+    if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  }
+  g_info = tara_run_info_t{p->mode, (int)dtype, bias_active, binding_active, parts, block_q, tara::kBlockK,
+                           grid, launches};
+  g_info_valid = true;
+  if (env_flag("TARA_LOG"))
+    std::fprintf(stderr, "[tara] %s %s B=%d H=%d N=%d D=%d bias=%d binding=%d parts=%d grid=%d launches=%d\n",
+                 partitioned ? "partitioned" : "fused", dtype == TARA_BF16 ? "bf16" : "fp32", B, H, N, D,
+                 (int)bias_active, (int)binding_active, parts, grid, launches);
+  return TARA_OK;
+}
+
+}  // extern "C"

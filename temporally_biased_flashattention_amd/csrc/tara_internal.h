@@ -1,0 +1,103 @@
+// Internal interface between the C ABI host code (tara_host.cpp) and the
+// gfx950 kernels (tara_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tara {
+
+constexpr int kBlockK = 64;          // keys per key tile (all paths)
+constexpr int kMaxParts = 64;        // == TARA_MAX_PARTITIONS
+constexpr int kMaxPictures = 16;     // == TARA_MAX_PICTURES
+
+// Kind of a key tile, from the per-key encodings (see MetaArgs):
+//  PLAIN   no key of the tile can carry a bias term
+//  GUIDE   every key is a biased guide key; lo/hi = min/max time (s)
+//  PICTURE every key is a picture key with the same log2 gain `bias`
+//  MIXED   anything else (per-element bias)
+enum : int { KT_PLAIN = 0, KT_GUIDE = 1, KT_PICTURE = 2, KT_MIXED = 3 };
+
+struct __attribute__((aligned(16))) KeyTileSummary {
+  int kind;
+  float lo;
+  float hi;
+  float bias;
+};
+
+// Per-token encodings written by the metadata kernel. The temporal rule is
+// evaluated in log2 units: with sigma = sqrt(strength * log2 e) / falloff,
+//   penalty * log2 e = min(max(|tq - tk| * sigma - w, 0)^2, cap2),
+// w = window * sigma, cap2 = cap * log2 e. Times stay in seconds so the gap
+// |tq - tk| is rounded relative to itself, not to the absolute times.
+//   tq[b][n]  time of a biased (target) query, NaN otherwise
+//   mq[b][n]  mask weight m of a target query when binding is active, else 0
+//   tk[b][n]  time of a biased (guide) key, NaN otherwise (n < npad)
+//   kb[b][n]  log2 gain of a bound picture key, else 0 (n < npad)
+// A NaN time makes the penalty 0 (fmaxf(NaN, 0) = 0), which is how unbiased
+// query/key pairs drop out of the per-element formula.
+struct MetaArgs {
+  const uint8_t* seg;
+  const float* time;
+  const int16_t* pic;
+  const float* mask;
+  int B, N, npad, nkt;
+  int bias_active, binding_active, num_pictures;
+  float lg2gain[kMaxPictures];
+  float* tq;
+  float* mq;
+  float* tk;
+  float* kb;
+  KeyTileSummary* ksum;   // [B][nkt]
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;           // fp32 path reads V directly
+  const __bf16* vt;        // bf16 path: V as [B*H][D][npad], keys contiguous
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  void* o;                 // fused: final O (input dtype)
+  float* lse;              // fused: final LSE [B][H][N]
+  float* opart;            // partitioned: O_p fp32 [P][B][H][N][D]
+  float* lsepart;          // partitioned: LSE_p [P][B][H][N]
+  int B, H, N, npad, nkt, nqb;
+  const float* tq;
+  const float* mq;
+  const float* tk;
+  const float* kb;
+  const KeyTileSummary* ksum;
+  float c;                 // softmax_scale * log2 e
+  float sigma;             // sqrt(strength * log2 e) / falloff  (1/s)
+  float w;                 // window * sigma
+  float cap2;              // cap * log2 e
+  float window;            // seconds: gaps <= window carry no penalty
+  float dsat;              // seconds: gaps >= window + falloff*sqrt(cap/strength) carry exactly cap
+  int nparts;
+  int kr[kMaxParts + 1];   // partition key offsets (fused: {0, N})
+};
+
+struct MergeArgs {
+  const float* opart;
+  const float* lsepart;
+  void* o;
+  float* lse;
+  int64_t o_sb, o_sh, o_sn;
+  int B, H, N, D, nparts;
+};
+
+hipError_t launch_meta(const MetaArgs& a, hipStream_t s);
+hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn, __bf16* vt,
+                             int B, int H, int N, int npad, int D, hipStream_t s);
+// Block of query rows per workgroup of the bf16 attention kernel.
+int attn_bf16_block_q(int D);
+int attn_bf16_grid(const AttnArgs& a);
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool partitioned, hipStream_t s);
+int attn_f32_block_q(int D);
+hipError_t launch_attn_f32(const AttnArgs& a, int D, bool partitioned, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, bool bf16_out, hipStream_t s);
+
+}  // namespace tara

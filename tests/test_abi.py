@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/tara.h
+declares, sizes workspaces, and rejects bad arguments on the host (argument
+errors are detected before any device work, so these calls never reach HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import temporally_biased_flashattention_amd as tara
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tara.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tara_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tara.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in tara.h but not exported"
+    assert sorted(tara.EXPORTED_SYMBOLS) == names
+
+
+def test_params_struct_matches_header_defaults():
+    p = tara.tara_params_default()
+    assert (p.window, p.falloff, p.strength, p.cap) == pytest.approx((0.20, 0.25, 2.0, 6.0))
+    assert p.binding_enabled == 0 and p.mode == tara.TARA_MODE_FUSED and p.num_partitions == 1
+    assert all(p.picture_gain[i] == 1.0 for i in range(16))
+    assert p.softmax_scale == 0.0
+    # ctypes layout: 4 floats, 2 ints, 16 floats, float, 2 ints, pointer
+    assert ctypes.sizeof(tara.TaraParams) == 4 * 4 + 2 * 4 + 16 * 4 + 4 + 2 * 4 + 4 + 8
+
+
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_bytes():
+    p = tara.tara_params_default()
+    B, H, N, D = 1, 2, 1000, 128
+    npad = 1024
+    nkt = npad // 64
+    meta = 2 * _al(B * N * 4) + 2 * _al(B * npad * 4) + _al(B * nkt * 16)
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p) == meta + _al(B * H * D * npad * 2)
+    assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, p) == meta
+    pp = tara.make_params(mode="partitioned", partitions=3)
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, pp) == (
+        meta + _al(B * H * D * npad * 2) + _al(3 * B * H * N * D * 4) + _al(3 * B * H * N * 4))
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, 0, H, N, D, p) == 0
+    with pytest.raises(tara.TaraError):
+        tara.tara_workspace_bytes(tara.TARA_BF16, 1, 1, 10, 96, p)
+    with pytest.raises(tara.TaraError):
+        tara.tara_workspace_bytes(7, 1, 1, 10, 64, p)
+
+
+# --------------------------------------------------------------- rejections
+FAKE = 0x10000          # never dereferenced: every call below fails host checks first
+
+
+def call(lib, params, dtype=tara.TARA_BF16, B=1, H=2, N=100, D=128, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
+         lse=FAKE, strides=None, seg=FAKE, time=FAKE, pic=FAKE, mask=0, ws=FAKE, ws_bytes=1 << 40):
+    if strides is None:
+        strides = (H * N * D, N * D, D)
+    s = [(ctypes.c_int64 * 3)(*strides) for _ in range(4)]
+    return lib.tara_attn_fwd(q, k, v, o, lse, dtype, B, H, N, D, s[0], s[1], s[2], s[3],
+                             seg, time, pic, mask or None, ctypes.byref(params) if params is not None else None,
+                             ws, ws_bytes, None)
+
+
+def test_rejections(lib):
+    P = tara.tara_params_default
+    assert call(lib, None) == -1
+    assert call(lib, P(), dtype=5) == -3
+    assert call(lib, P(), D=96) == -4
+    assert call(lib, P(), N=-1) == -2
+    assert call(lib, P(), B=300, H=300) == -2
+    assert call(lib, P(), q=0) == -1
+    assert call(lib, P(), seg=0) == -1
+    assert call(lib, P(), q=FAKE + 8) == -5                      # base not 16-byte aligned
+    assert call(lib, P(), strides=(1000 * 128, 100 * 128, 130)) == -5   # row stride not x8
+    assert call(lib, P(), dtype=tara.TARA_FP32, strides=(800, 400, 6)) == -5
+    assert call(lib, P(), ws_bytes=10) == -7
+    assert call(lib, P(), ws=0) == -7
+    assert call(lib, P(), ws=FAKE + 64) == -7                    # not 256-byte aligned
+    assert call(lib, tara.make_params(falloff=0.0)) == -6
+    assert call(lib, tara.make_params(falloff=-1.0)) == -6
+    assert call(lib, tara.make_params(window=-0.1)) == -6
+    assert call(lib, tara.make_params(strength=-1.0)) == -6
+    assert call(lib, tara.make_params(cap=-1.0)) == -6
+    assert call(lib, tara.make_params(cap=float("inf"))) == -6
+    assert call(lib, tara.make_params(window=float("nan"))) == -6
+    assert call(lib, tara.make_params(binding=True, gains=(1.25, 0.0))) == -6
+    assert call(lib, tara.make_params(binding=True, gains=(1.25, -2.0))) == -6
+    assert call(lib, tara.make_params(softmax_scale=-1.0)) == -6
+    assert call(lib, tara.make_params(binding=True, gains=(1.25,)), pic=0) == -1   # ids needed
+    assert call(lib, tara.make_params(mode="partitioned", partitions=0)) == -6
+    assert call(lib, tara.make_params(mode="partitioned", partitions=65)) == -6
+    assert call(lib, tara.make_params(mode="partitioned", partitions=2, bounds=(0, 50, 99))) == -6
+    assert call(lib, tara.make_params(mode="partitioned", partitions=2, bounds=(0, 60, 50))) == -6
+    assert call(lib, tara.make_params(mode="partitioned", partitions=2, bounds=(1, 50, 100))) == -6
+    p = P()
+    p.mode = 7
+    assert call(lib, p) == -6
+
+
+def test_messages(lib):
+    call(lib, tara.make_params(falloff=0.0))
+    assert "falloff" in tara.tara_last_error()
+    for st in range(0, -10, -1):
+        assert tara.tara_status_string(st) and tara.tara_status_string(st) != "unknown status"
+    assert tara.tara_status_string(-99) == "unknown status"
+
+
+def test_empty_calls_are_ok_without_device_work(lib):
+    # B, H or N == 0: valid, nothing enqueued (no HIP call is made)
+    assert call(lib, tara.tara_params_default(), N=0, q=0, k=0, v=0, o=0, lse=0, ws=0) == 0
+    assert call(lib, tara.tara_params_default(), B=0, q=0, k=0, v=0, o=0, lse=0, ws=0) == 0
+    info = tara.tara_get_last_run_info()
+    assert info["launches"] == 0 and info["block_k"] == 64
+
+
+def test_timing_read_empty(lib):
+    tara.tara_timing_enable(False)
+    assert tara.tara_timing_read() == []

@@ -1,0 +1,167 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle,
+element by element, at sizes the oracle finishes in seconds that still span
+several 64-key tiles, several 128-row query blocks and a ragged tail.
+
+Gates: max|dO| <= 1e-2, max|dLSE| <= 1e-3, ||dO||/||O|| <= 1e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import tara_inputs as ti
+from tara_testlib import (compare, log, qkv_random, run_gpu, run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+DEF = ti.Params()
+BIND = ti.Params(window=0.10, falloff=0.40, strength=3.0, cap=8.0, binding=True, gains=(1.25, 0.75, 0.75))
+
+
+def small_layout(mask=False, pictures=2):
+    # 6 latent frames of 6x10 target/guide patches: 360 + 360 + pictures x 40 + 37 text
+    return ti.make_layout(6, (6, 10), (6, 10), pictures, 40, 37, mask=mask)
+
+
+def framed_layout(mask=False):
+    # 12 latent frames of 8x16 patches: whole 64-key tiles per frame, so most
+    # guide tiles take the constant (saturated / inside-window) classes
+    return ti.make_layout(12, (8, 16), (8, 16), 3, 100, 50, mask=mask)
+
+
+def check(q, k, v, lay, p, what, **kw):
+    o, l = run_gpu(q, k, v, lay, p, **kw)
+    rkw = {}
+    if "softmax_scale" in kw and kw["softmax_scale"]:
+        rkw["softmax_scale"] = kw["softmax_scale"]
+    if kw.get("use_mask") is False:
+        rkw["use_mask"] = False
+    ro, rl = run_oracle(q, k, v, lay, p, **rkw)
+    return compare(o.numpy(), l.numpy(), ro, rl, what=what)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+
+def test_config1_fp32_all_rows():
+    cfg = ti.config(1)
+    lay = cfg.layout()
+    q, k, v = ti.qkv(cfg)
+    check(q, k, v, lay, cfg.params, "config1 fp32 fused")
+    check(q, k, v, lay, cfg.params, "config1 fp32 partitioned", mode="partitioned", partitions=3)
+
+
+def test_uniform_scores_q0():
+    lay = small_layout()
+    q, k, v = qkv_random(1, 2, lay.n, 128, seed=1)
+    q = torch.zeros_like(q)
+    check(q, k, v, lay, DEF, "q=0 defaults")
+
+
+def test_plain_attention_strength0():
+    lay = small_layout()
+    q, k, v = qkv_random(1, 2, lay.n, 128, seed=2)
+    check(q, k, v, lay, ti.Params(strength=0.0), "strength=0")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_defaults_small(d):
+    lay = small_layout()
+    q, k, v = qkv_random(1, 3, lay.n, d, seed=3 + d)
+    check(q, k, v, lay, DEF, f"defaults d={d}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_binding_mask_small(d):
+    lay = small_layout(mask=True, pictures=3)
+    q, k, v = qkv_random(1, 2, lay.n, d, seed=5 + d)
+    check(q, k, v, lay, BIND, f"binding+mask d={d}")
+    check(q, k, v, lay, BIND, f"binding no mask d={d}", use_mask=False)
+
+
+def test_framed_tile_classes():
+    lay = framed_layout(mask=True)
+    q, k, v = qkv_random(1, 2, lay.n, 128, seed=7)
+    check(q, k, v, lay, DEF, "framed defaults")
+    check(q, k, v, lay, BIND, "framed binding")
+
+
+def test_shuffled_order():
+    rng = np.random.default_rng(8)
+    base = small_layout(mask=True, pictures=3)
+    lay = base.permuted(rng.permutation(base.n))
+    q, k, v = qkv_random(1, 2, lay.n, 128, seed=8)
+    check(q, k, v, lay, BIND, "shuffled binding")
+
+
+def test_bnhd_strides_and_batch():
+    lay = small_layout(mask=True, pictures=3)
+    q, k, v = qkv_random(2, 2, lay.n, 128, seed=9)
+    check(q, k, v, lay, BIND, "bnhd B=2", layout="bnhd")
+
+
+def test_temperature_q_k_scaled():
+    """Peaky softmax (scores ~ N(0, 16)): O is close to single rows of V, so
+    bf16 rounding of O itself reaches |O| * 2^-9. Element gate derived from the
+    arithmetic: P and O each rounded to bf16 (<= 2^-9 max|V| each), doubled for
+    margin: 2^-7 max|V|. LSE and relative gates unchanged."""
+    lay = framed_layout()
+    q, k, v = qkv_random(1, 2, lay.n, 128, seed=10, scale=2.0)
+    o, l = run_gpu(q, k, v, lay, DEF)
+    ro, rl = run_oracle(q, k, v, lay, DEF)
+    compare(o.numpy(), l.numpy(), ro, rl, tol_o=2.0 ** -7 * float(v.float().abs().max()),
+            what="q,k ~ N(0,4)")
+
+
+@pytest.mark.parametrize("parts,bounds", [(3, None), (1, None), (4, "segments"), (5, "ragged")])
+def test_partitioned_matches(parts, bounds):
+    lay = small_layout(mask=True, pictures=3)
+    n = lay.n
+    if bounds == "segments":
+        nt = int((lay.seg == ti.SEG_TARGET).sum())
+        ng = int((lay.seg == ti.SEG_GUIDE).sum())
+        npic = int((lay.seg == ti.SEG_PICTURE).sum())
+        b = [0, nt, nt + ng, nt + ng + npic, n]
+    elif bounds == "ragged":
+        b = [0, 1, 100, 100, 777, n]
+    else:
+        b = None
+    q, k, v = qkv_random(1, 2, n, 128, seed=11)
+    res = check(q, k, v, lay, BIND, f"partitioned P={parts} {bounds}", mode="partitioned",
+                partitions=parts, bounds=b)
+    of, lf = run_gpu(q, k, v, lay, BIND)
+    op, lp = run_gpu(q, k, v, lay, BIND, mode="partitioned", partitions=parts, bounds=b)
+    log(f"fused vs partitioned: max|dO|={float((of - op).abs().max()):.3e} "
+        f"max|dLSE|={float((lf - lp).abs().max()):.3e}")
+    assert float((lf - lp).abs().max()) <= 1e-3
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 200])
+def test_tiny_and_boundary_lengths(n):
+    rng = np.random.default_rng(100 + n)
+    lay = ti.random_layout(rng, n, frames=4, pictures=2, mask=True)
+    q, k, v = qkv_random(1, 2, n, 128, seed=12 + n)
+    p = ti.Params(binding=True, gains=(1.5, 0.6))
+    check(q, k, v, lay, p, f"n={n}")
+
+
+def test_fp32_d128_and_softmax_scale():
+    lay = small_layout(mask=True, pictures=3)
+    q, k, v = qkv_random(1, 2, lay.n, 128, seed=13, dtype=torch.float32)
+    check(q, k, v, lay, BIND, "fp32 d=128")
+    q, k, v = qkv_random(1, 2, lay.n, 128, seed=14)
+    check(q, k, v, lay, DEF, "bf16 scale 0.05", softmax_scale=0.05)
+
+
+def test_segment_extremes():
+    n = 700
+    q, k, v = qkv_random(1, 2, n, 128, seed=15)
+    for name, seg in (("all target", ti.SEG_TARGET), ("all guide", ti.SEG_GUIDE), ("all other", ti.SEG_OTHER)):
+        lay = ti.make_layout(7, (10, 10), (0, 0), 0, 0, 0)
+        lay.seg[:] = seg
+        check(q, k, v, lay, DEF, name)
