@@ -1,0 +1,214 @@
+"""Throughput of TARA attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5] [--mode fused|partitioned]
+
+A step is one tara_attn_fwd call (metadata encoding, V layout pass, the fused
+attention kernel; plus the merge in partitioned mode) over the whole workload,
+inputs already resident in HBM. The default workload is the 107,126-token
+packed sequence (52,751 target + 52,751 guide + 2 x 556 picture + 512 text
+tokens, 107 latent frames) at 56 heads of dim 128 in bf16 with the default
+TARA controls. Prints one JSON line.
+
+Effective work per step is 4 * B * H * N^2 * D FLOP (both products over every
+query/key pair; bias skipping removes no contraction work).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
+PEAK_FP32_VALU_TFLOPS = 157.3
+METRIC = "TARA attention TFLOP/s and % of bf16 MFMA peak at 107,126 tok × 56 heads"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_headline_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "temporally_biased_flashattention_amd", "csrc", "tara_kernels.hip")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload(name):
+    import tara_inputs as ti
+    cid = 6 if name == "headline" else int(name)
+    return ti.config(cid)
+
+
+def measured_traffic(per_launch_flop_unit):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, q, k, v, lay, seconds: float):
+    """The fp64 oracle (as it stands) on a bounded, stratified sample of query
+    rows of head 0, timed on the host cores; scaled to effective TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    from tests.tara_testlib import sample_rows
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 0)) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    rows = sample_rows(lay, n_random=30000, per_segment=512, seed=1)
+    rng = np.random.default_rng(2)
+    rows = rng.permutation(rows)
+    qh, kh, vh = (x[0, 0].float().numpy() for x in (q, k, v))
+    p = cfg.params.f32()
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(rows) and time.perf_counter() - t0 < seconds:
+        r = np.sort(rows[done:done + 128])
+        oracle.attention_head(qh, kh, vh, lay.seg, lay.time, lay.picture, lay.mask, p, rows=r)
+        done += len(r)
+    dt = time.perf_counter() - t0
+    flop = oracle.flops(1, 1, lay.n, cfg.head_dim, rows=done)
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} stratified query rows of head 0 of {cfg.name} against all {lay.n} keys, "
+                      f"fp64 NumPy oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--mode", default="fused", choices=["fused", "partitioned"])
+    ap.add_argument("--partitions", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this many GiB (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); "
+              "TARA attention here is a single-GPU kernel and no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tara_inputs as ti
+    import temporally_biased_flashattention_amd as tara
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    tara.load_library()
+    cfg = workload(args.workload)
+    lay = cfg.layout()
+    B, H, N, D = 1, cfg.heads, lay.n, cfg.head_dim
+    log(f"workload {cfg.name}: N={N} H={H} D={D} dtype={cfg.dtype}; generating inputs")
+    t0 = time.perf_counter()
+    q, k, v = ti.qkv(cfg)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    seg = torch.from_numpy(lay.seg)[None].to(dev)
+    tim = torch.from_numpy(lay.time)[None].to(dev)
+    pic = torch.from_numpy(lay.picture)[None].to(dev)
+    mask = None if lay.mask is None else torch.from_numpy(lay.mask)[None].to(dev)
+    cp = cfg.params
+    params = tara.make_params(window=cp.window, falloff=cp.falloff, strength=cp.strength, cap=cp.cap,
+                              binding=cp.binding, gains=tuple(cp.gains), mode=args.mode,
+                              partitions=args.partitions if args.mode == "partitioned" else 1)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(tara.tara_workspace_bytes(tara.TARA_BF16 if cfg.dtype == "bf16" else tara.TARA_FP32,
+                                                   B, H, N, D, params), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        tara.tara_attn_fwd(qd, kd, vd, o, lse, seg, tim, pic, mask, params, ws)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    tara.tara_timing_read()
+    tara.tara_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tara.tara_timing_enable(False)
+    kms = tara.tara_timing_read()
+    log(f"{args.steps} timed steps in {elapsed:.3f} s")
+    info = tara.tara_get_last_run_info()
+
+    if args.copy_calib_gib > 0:
+        nb = int(args.copy_calib_gib * (1 << 30))
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {nb} bytes")
+        del src, dst
+
+    flop = 4.0 * B * H * float(N) * N * D
+    ms_step = elapsed / args.steps * 1e3
+    value = flop / (ms_step / 1e3) / 1e12
+    k_avg = sum(kms) / len(kms) if kms else float("nan")
+    achieved = flop / (k_avg / 1e3) / 1e12
+    traffic = measured_traffic(flop)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, packed H3-shaped metadata)",
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": f"{cfg.name} ({args.mode})", "tokens": N, "heads": H, "head_dim": D, "batch": B,
+                   "target_tokens": int((lay.seg == 0).sum()), "guide_tokens": int((lay.seg == 1).sum()),
+                   "mode": args.mode, "partitions": info.get("num_partitions"),
+                   "controls": {"window": cfg.params.window, "falloff": cfg.params.falloff,
+                                "strength": cfg.params.strength, "cap": cfg.params.cap,
+                                "binding": cfg.params.binding, "gains": list(cfg.params.gains)},
+                   "block_q": info.get("block_q"), "block_k": info.get("block_k"), "grid": info.get("grid")},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
+                     "kernel_ms_avg": round(k_avg, 4), "launches_timed": len(kms),
+                     "flop_per_launch": flop},
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(cfg, q, k, v, lay, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

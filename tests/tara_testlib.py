@@ -48,8 +48,9 @@ def device_meta(lay: ti.Layout, device="cuda", batch=1):
 
 
 def run_gpu(q, k, v, lay: ti.Layout, p: ti.Params, mode="fused", partitions=1, bounds=None,
-            softmax_scale=0.0, layout="bhnd", use_mask=True):
-    """q, k, v: CPU tensors [B, H, N, D]. Returns (O fp32 CPU, LSE fp32 CPU)."""
+            softmax_scale=0.0, layout="bhnd", use_mask=True, heads=None, rows=None):
+    """q, k, v: CPU tensors [B, H, N, D]. Returns (O fp32 CPU, LSE fp32 CPU),
+    restricted to the given heads and query rows when those are given."""
     dev = "cuda"
     B = q.shape[0]
     if layout == "bhnd":
@@ -60,6 +61,13 @@ def run_gpu(q, k, v, lay: ti.Layout, p: ti.Params, mode="fused", partitions=1, b
     params = tara_params(p, mode, partitions, bounds, softmax_scale)
     o, lse = tara.attn_fwd(qd, kd, vd, seg, tim, pic, mask if use_mask else None, params)
     torch.cuda.synchronize()
+    del qd, kd, vd
+    if heads is not None:
+        hi = torch.tensor(list(heads), device=dev)
+        o, lse = o.index_select(1, hi), lse.index_select(1, hi)
+    if rows is not None:
+        ri = torch.as_tensor(np.asarray(rows), device=dev)
+        o, lse = o.index_select(2, ri), lse.index_select(2, ri)
     return o.float().cpu(), lse.cpu()
 
 

@@ -1,0 +1,101 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (all heads, one fused call; partitioned for the binding
+workload too), checked on stratified samples of query rows of three heads
+against the fp64 oracle. Full-scale Q = 0 probes make the attention weights a
+function of the bias alone, so per-segment attention mass checks the temporal
+and binding terms at full size with a tight gate.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tara_inputs as ti
+from tara_testlib import compare, log, run_gpu, run_oracle, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _heads(h):
+    return sorted({0, h // 2, h - 1})
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6])
+def test_fullsize_sampled_rows(cid):
+    cfg = ti.config(cid)
+    lay = cfg.layout()
+    log(f"config {cid} {cfg.name}: N={lay.n} H={cfg.heads}; generating inputs")
+    q, k, v = ti.qkv(cfg)
+    heads = _heads(cfg.heads)
+    rows = sample_rows(lay, n_random=256, per_segment=64, seed=cid)
+    log(f"running GPU (all {cfg.heads} heads), comparing {len(rows)} rows x heads {heads}")
+    o, l = run_gpu(q, k, v, lay, cfg.params, heads=heads, rows=rows)
+    ro, rl = run_oracle(q, k, v, lay, cfg.params, rows=rows, heads=heads)
+    compare(o.numpy(), l.numpy(), ro, rl, what=f"config {cid} fused sampled")
+
+
+def test_fullsize_binding_partitioned():
+    cfg = ti.config(5)
+    lay = cfg.layout()
+    q, k, v = ti.qkv(cfg, heads=[0, 1])
+    n = lay.n
+    nt = int((lay.seg == ti.SEG_TARGET).sum())
+    ng = int((lay.seg == ti.SEG_GUIDE).sum())
+    bounds = [0, nt, nt + ng, n]          # target | guide | pictures + text
+    rows = sample_rows(lay, n_random=256, per_segment=64, seed=55)
+    o, l = run_gpu(q, k, v, lay, cfg.params, mode="partitioned", partitions=3, bounds=bounds, rows=rows)
+    ro, rl = run_oracle(q, k, v, lay, cfg.params, rows=rows)
+    compare(o.numpy(), l.numpy(), ro, rl, what="config 5 partitioned (segment bounds) sampled")
+    of, lf = run_gpu(q, k, v, lay, cfg.params, rows=rows)
+    dl = float((lf - l).abs().max())
+    log(f"fused vs partitioned at full size: max|dLSE|={dl:.3e} max|dO|={float((of - o).abs().max()):.3e}")
+    assert dl <= 1e-3
+
+
+def _probe_v(lay, d):
+    v = torch.zeros(1, 2, lay.n, d)
+    v[0, :, lay.seg == ti.SEG_GUIDE, 0] = 1.0
+    v[0, :, lay.seg == ti.SEG_PICTURE, 1] = 1.0
+    v[0, :, :, 2] = 1.0
+    for i in range(3):
+        v[0, :, lay.picture == i, 3 + i] = 1.0
+    return v.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("cid", [4, 5, 6])
+def test_fullsize_q0_probe(cid):
+    """Q = 0: every logit is its bias, so LSE and the guide / picture attention
+    mass of each row are fixed by the rule. LSE gate 1e-4. Mass gate 2^-7
+    relative + 1e-6: each unnormalised weight is rounded to bf16 (unit
+    roundoff 2^-8) before the P.V product, and all keys of one frame or picture
+    share that rounding; the fp32 normaliser adds at most the LSE error; the
+    bound is doubled for margin."""
+    cfg = ti.config(cid)
+    lay = cfg.layout()
+    g = torch.Generator().manual_seed(900 + cid)
+    k = torch.randn(1, 2, lay.n, cfg.head_dim, generator=g).to(torch.bfloat16)
+    q = torch.zeros_like(k)
+    v = _probe_v(lay, cfg.head_dim)
+    rows = sample_rows(lay, n_random=512, per_segment=64, seed=cid)
+    o, l = run_gpu(q, k, v, lay, cfg.params, rows=rows)
+    ro, rl = run_oracle(q, k, v, lay, cfg.params, rows=rows)
+    dl = float(np.abs(l.numpy() - rl).max())
+    mass = ro[..., :6]
+    dm = np.abs(o.numpy()[..., :6] - mass)
+    bad = dm > 2.0 ** -7 * mass + 1e-6
+    if bad.any():
+        for idx in np.argwhere(bad)[:10]:
+            b, h, r, c = (int(x) for x in idx)
+            row = int(rows[r])
+            log(f"  off: head {h} row {row} seg {lay.seg[row]} col {c}: gpu {o.numpy()[b, h, r, c]:.6e} "
+                f"ref {mass[b, h, r, c]:.6e} m={None if lay.mask is None else lay.mask[row]}")
+    log(f"config {cid} Q=0 probe: max|dLSE|={dl:.3e} max|dmass|={dm.max():.3e} "
+        f"guide mass range [{mass[..., 0].min():.4f}, {mass[..., 0].max():.4f}] "
+        f"picture mass range [{mass[..., 1].min():.4f}, {mass[..., 1].max():.4f}]")
+    assert dl <= 1e-4
+    assert not bad.any(), f"{int(bad.sum())} mass entries off"

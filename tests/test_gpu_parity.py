@@ -107,14 +107,15 @@ def test_bnhd_strides_and_batch():
 
 def test_temperature_q_k_scaled():
     """Peaky softmax (scores ~ N(0, 16)): O is close to single rows of V, so
-    bf16 rounding of O itself reaches |O| * 2^-9. Element gate derived from the
-    arithmetic: P and O each rounded to bf16 (<= 2^-9 max|V| each), doubled for
-    margin: 2^-7 max|V|. LSE and relative gates unchanged."""
+    bf16 rounding of O itself reaches |O| * 2^-8. Element gate derived from the
+    arithmetic: P and O each rounded to bf16 (unit roundoff 2^-8, so at most
+    2^-8 max|V| each), doubled for margin: 2^-6 max|V|. LSE and relative gates
+    unchanged."""
     lay = framed_layout()
     q, k, v = qkv_random(1, 2, lay.n, 128, seed=10, scale=2.0)
     o, l = run_gpu(q, k, v, lay, DEF)
     ro, rl = run_oracle(q, k, v, lay, DEF)
-    compare(o.numpy(), l.numpy(), ro, rl, tol_o=2.0 ** -7 * float(v.float().abs().max()),
+    compare(o.numpy(), l.numpy(), ro, rl, tol_o=2.0 ** -6 * float(v.float().abs().max()),
             what="q,k ~ N(0,4)")
 
 
