@@ -179,68 +179,175 @@ hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn
 }
 
 // --------------------------------------------------------- bf16 MFMA kernel
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kQW = 32;                   // query rows per wave
-constexpr int kBQ = kWaves * kQW;         // query rows per workgroup
+// One workgroup = NW waves x 32 query rows of one (batch, head). Per 64-key
+// tile t every wave runs a two-phase software pipeline so that its MFMAs and
+// its softmax VALU work interleave in program order (MFMA and VALU of one wave
+// co-issue; in-order issue means the VALU work has to sit between the MFMAs):
+//   phase A: S_{t+1} = K_{t+1} Q^T (16 MFMAs)   with   P_t = exp2(X_t), row sums, bf16 pack
+//   phase B: O^T += V_t^T P_t^T (16 MFMAs)      with   max / bias class / X_{t+1} = S_{t+1} c + b - m
+// so K runs one tile ahead of V in LDS: iteration t reads K_{t+1} and V_t and
+// stages K_{t+2} and V_{t+1} (two LDS buffers each, one barrier per tile).
 
 // Key row held by S^T output row `r` of a 32-key block: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Global -> registers part of staging one key tile: K rows [kt*64, kt*64+64)
-// (rows past N clamped to N-1; those keys are masked later) and the matching
-// 64 key columns of V^T (zero-padded to npad).
-template <int D, int NT, int KCH, int VCH>
-__device__ __forceinline__ void load_kv_tile(u32x4 (&pk)[KCH], u32x4 (&pv)[VCH], const __bf16* kg,
-                                             int64_t k_sn, const __bf16* vg, int npad, int kt, int N,
-                                             int tid) {
+template <int D, int NT, int KCH>
+__device__ __forceinline__ void load_k_tile(u32x4 (&pk)[KCH], const char* kg_tile, const uint32_t (&koff)[KCH],
+                                            const int (&krow)[KCH], int rows_left, int64_t k_sn_bytes) {
+  // rows beyond the sequence (tail tile) re-read its last row; their keys are masked
+  if (rows_left >= kBlockK) {
 #pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int c = tid + i * NT;
-    const int r = c / (D / 8), c8 = c % (D / 8);
-    const int n = min(kt * kBlockK + r, N - 1);
-    pk[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)n * k_sn + c8 * 8);
-  }
+    for (int i = 0; i < KCH; ++i) pk[i] = *reinterpret_cast<const u32x4*>(kg_tile + koff[i]);
+  } else {
 #pragma unroll
-  for (int i = 0; i < VCH; ++i) {
-    const int c = tid + i * NT;
-    const int d = c / (kBlockK / 8), c8 = c % (kBlockK / 8);
-    pv[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)d * npad + kt * kBlockK + c8 * 8);
+    for (int i = 0; i < KCH; ++i) {
+      const int extra = krow[i] - min(krow[i], rows_left - 1);
+      pk[i] = *reinterpret_cast<const u32x4*>(kg_tile + koff[i] - (int64_t)extra * k_sn_bytes);
+    }
   }
 }
 
-// Registers -> LDS part: K tile as [64][KROW], V^T tile as [D][VROW].
-template <int D, int NT, int KCH, int VCH, int KROW, int VROW>
-__device__ __forceinline__ void store_kv_tile(const u32x4 (&pk)[KCH], const u32x4 (&pv)[VCH], __bf16* ks,
-                                              __bf16* vs, int tid) {
+template <int VCH>
+__device__ __forceinline__ void load_v_tile(u32x4 (&pv)[VCH], const char* vg_tile, const uint32_t (&voff)[VCH]) {
 #pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int c = tid + i * NT;
-    const int r = c / (D / 8), c8 = c % (D / 8);
-    *reinterpret_cast<u32x4*>(ks + r * KROW + c8 * 8) = pk[i];
-  }
+  for (int i = 0; i < VCH; ++i) pv[i] = *reinterpret_cast<const u32x4*>(vg_tile + voff[i]);
+}
+
+template <int N>
+__device__ __forceinline__ void store_tile(const u32x4 (&p)[N], __bf16* lds, const uint32_t (&soff)[N]) {
 #pragma unroll
-  for (int i = 0; i < VCH; ++i) {
-    const int c = tid + i * NT;
-    const int d = c / (kBlockK / 8), c8 = c % (kBlockK / 8);
-    *reinterpret_cast<u32x4*>(vs + d * VROW + c8 * 8) = pv[i];
+  for (int i = 0; i < N; ++i) *reinterpret_cast<u32x4*>(lds + soff[i]) = p[i];
+}
+
+// S^T for the two 32-key blocks of a K tile in LDS.
+template <int D, int KROW>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const __bf16* ks, int krow_lane, int hh,
+                                        const bf16x8 (&qf)[D / 16]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16{};
+    const __bf16* kr = ks + (kb * 32 + krow_lane) * KROW + hh * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + kk * 16), qf[kk],
+                                                      s[kb], 0, 0, 0);
   }
 }
 
-template <int D, bool PART>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// i-th K fragment of phase A: key block i & 1, head-dim step i >> 1.
+template <int KROW>
+__device__ __forceinline__ bf16x8 kfrag(const __bf16* kr0, int i) {
+  return *reinterpret_cast<const bf16x8*>(kr0 + (i & 1) * 32 * KROW + (i >> 1) * 16);
+}
+
+// i-th V^T fragment of phase B: 32-row block i % NDB of the head dim, 16-key
+// chunk i / NDB (key block kb = chunk / 2, half c2 = chunk % 2).
+template <int VROW, int NDB>
+__device__ __forceinline__ bf16x8 vfrag(const __bf16* vr0, int i) {
+  return *reinterpret_cast<const bf16x8*>(vr0 + (i % NDB) * 32 * VROW + (i / NDB) * 16);
+}
+
+// max of three floats as one v_max3_f32. The operands here are scores (finite,
+// or -inf for masked keys), so the NaN quieting that fmaxf adds around MFMA
+// results (one extra v_max_f32 per operand) is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+typedef const __attribute__((address_space(4))) KeyTileSummary* KsumConstPtr;
+
+// Uniform load of a tile summary through the constant address space (scalar loads).
+__device__ __forceinline__ KeyTileSummary load_summary(KsumConstPtr p, int i) {
+  KeyTileSummary r;
+  r.kind = p[i].kind;
+  r.lo = p[i].lo;
+  r.hi = p[i].hi;
+  r.bias = p[i].bias;
+  return r;
+}
+
+// Bias class of one key tile for this wave: returns true when the tile needs
+// the per-element formula; otherwise *brow is the lane's constant bias (log2).
+__device__ __forceinline__ bool tile_class(const KeyTileSummary& sm, bool partial, bool qbiased, float tq, float mq,
+                                           const AttnArgs& a, float* brow) {
+  float b = 0.0f;
+  bool lane_elem = partial;
+  if (!partial) {
+    if (sm.kind == KT_GUIDE) {
+      if (qbiased) {
+        const float dlo = sm.lo - tq, dhi = tq - sm.hi;
+        const float dmin = fmaxf(fmaxf(dlo, dhi), 0.0f);
+        const float dmax = fmaxf(-dlo, -dhi);
+        if (dmin >= a.dsat) b = -a.cap2;
+        else if (!(dmax <= a.window)) lane_elem = true;
+      }
+    } else if (sm.kind == KT_PICTURE) {
+      b = mq * sm.bias;
+    } else if (sm.kind == KT_MIXED) {
+      lane_elem = true;
+    }
+  }
+  *brow = b;
+  return wave_any(lane_elem);
+}
+
+// Per-element bias of a key tile, in place: x = s*c + m*log2(gain) - penalty,
+// keys outside [k0, k1) -> -inf. Lane half hh holds keys 8*hh..8*hh+7 and
+// 16+8*hh..16+8*hh+7 of each 32-key block.
+__device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, float tq, float mq, bool partial, int k0,
+                                          int k1, const float* tkb, const float* kbb, const AttnArgs& a) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int kx = kbase + kb * 32 + c2 * 16 + hh * 8;
+      const f32x4 t0 = *reinterpret_cast<const f32x4*>(tkb + kx);
+      const f32x4 t1 = *reinterpret_cast<const f32x4*>(tkb + kx + 4);
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(kbb + kx);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(kbb + kx + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float tk = e < 4 ? t0[e] : t1[e - 4];
+        const float gk = e < 4 ? g0[e] : g1[e - 4];
+        const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);   // NaN time -> 0
+        const float pen = fminf(dd * dd, a.cap2);
+        float x = fmaf(s[kb][c2 * 8 + e], a.c, fmaf(mq, gk, -pen));
+        if (partial && (kx + e < k0 || kx + e >= k1)) x = -INFINITY;
+        s[kb][c2 * 8 + e] = x;
+      }
+    }
+  }
+}
+
+template <int D, int NW, bool PART>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NT = kWaves * 64;
+  constexpr int NT = NW * 64;
+  constexpr int BQ = NW * 32;
   constexpr int KROW = D + 8;              // padded LDS pitch of a K row (elements)
   constexpr int VROW = kBlockK + 8;        // padded LDS pitch of a V^T row (elements)
   constexpr int KTILE = kBlockK * KROW;
   constexpr int VTILE = D * VROW;
-  constexpr int STAGE = KTILE + VTILE;
   constexpr int KCH = kBlockK * D / 8 / NT;   // 16-byte chunks per thread, K tile
   constexpr int VCH = D * kBlockK / 8 / NT;   // 16-byte chunks per thread, V^T tile
-  constexpr int NKK = D / 16;                 // MFMA k-steps over the head dim
-  constexpr int NDB = D / 32;                 // 32-row blocks of O^T
+  constexpr int NKK = D / 16;
+  constexpr int NDB = D / 32;
   static_assert(KCH * NT * 8 == kBlockK * D && VCH * NT * 8 == kBlockK * D, "tile split");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * KTILE + 2 * VTILE];
+  // LDS: K buffers 0/1 then V^T buffers 0/1
+#define KBUF(i) (smem + (i) * KTILE)
+#define VBUF(i) (smem + 2 * KTILE + (i) * VTILE)
 
   const int part = PART ? blockIdx.y : 0;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -249,7 +356,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int N = a.N;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
-  const int qrow = qblk * kBQ + wave * kQW + lq;
+  const int qrow = qblk * BQ + wave * 32 + lq;
   const bool qvalid = qrow < N;
   const int qr = qvalid ? qrow : N - 1;
 
@@ -262,163 +369,222 @@ void attn_bf16_kernel(AttnArgs a) {
   const bool qbiased = tq == tq;
 
   const int k0 = a.kr[part], k1 = a.kr[part + 1];
-  // an empty key range visits no tile (a range inside one tile would
-  // otherwise mask every key of it)
-  const int kt0 = k0 / kBlockK, kt1 = k1 > k0 ? (k1 + kBlockK - 1) / kBlockK : kt0;
+  if (k1 <= k0) {
+    // empty key range (partitioned mode only): contributes nothing to the merge
+    if (PART && qvalid) {
+      float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
+      if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = -INFINITY;
+    }
+    return;
+  }
+  const int kt0 = k0 / kBlockK, kt1 = (k1 + kBlockK - 1) / kBlockK;
+
+  // staging addresses: 32-bit byte offsets from a per-tile scalar base
+  const char* kg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh);
+  const char* vg = reinterpret_cast<const char*>(a.vt + (int64_t)bh * D * a.npad);
+  const int64_t k_sn_bytes = a.k_sn * 2;
+  uint32_t koff[KCH], ksoff[KCH], voff[VCH], vsoff[VCH];
+  int krow[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int c = tid + i * NT, r = c / (D / 8), c8 = c % (D / 8);
+    krow[i] = r;
+    koff[i] = (uint32_t)(r * k_sn_bytes + c8 * 16);
+    ksoff[i] = r * KROW + c8 * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < VCH; ++i) {
+    const int c = tid + i * NT, d = c / (kBlockK / 8), c8 = c % (kBlockK / 8);
+    voff[i] = (uint32_t)((d * a.npad + c8 * 8) * 2);
+    vsoff[i] = d * VROW + c8 * 8;
+  }
+  auto ktile_base = [&](int kt) { return kg + (int64_t)kt * kBlockK * k_sn_bytes; };
+  auto vtile_base = [&](int kt) { return vg + (int64_t)kt * kBlockK * 2; };
+
+  const float* tkb = a.tk + (int64_t)b * a.npad;
+  const float* kbb = a.kb + (int64_t)b * a.npad;
+  const KeyTileSummary* ks_b = a.ksum + (int64_t)b * a.nkt;
+  // the same summaries through the constant address space: uniform loads of
+  // them become scalar loads
+  const KsumConstPtr ks_c = (KsumConstPtr)ks_b;
+  const int krow_lane = perm32(lq);
+  KeyTileSummary sm_next;
 
   f32x16 o[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m_used = -INFINITY, lsum = 0.0f;
-
-  const __bf16* kg = static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const __bf16* vg = a.vt + (int64_t)bh * D * a.npad;
-  const float* tkb = a.tk + (int64_t)b * a.npad;
-  const float* kbb = a.kb + (int64_t)b * a.npad;
-  const KeyTileSummary* ks_b = a.ksum + (int64_t)b * a.nkt;
-
+  f32x16 x[2];   // X_t = S_t * c + bias - m_used (exp2 argument)
   u32x4 pk[KCH], pv[VCH];
-  if (kt0 < kt1) {
-    load_kv_tile<D, NT, KCH, VCH>(pk, pv, kg, a.k_sn, vg, a.npad, kt0, N, tid);
-    store_kv_tile<D, NT, KCH, VCH, KROW, VROW>(pk, pv, smem, smem + KTILE, tid);
+
+  {
+    // prologue: K_t0, V_t0 staged; S_t0; X_t0; K_{t0+1} staged
+    load_k_tile<D, NT, KCH>(pk, ktile_base(kt0), koff, krow, N - kt0 * kBlockK, k_sn_bytes);
+    load_v_tile<VCH>(pv, vtile_base(kt0), voff);
+    store_tile<KCH>(pk, KBUF(0), ksoff);
+    store_tile<VCH>(pv, VBUF(0), vsoff);
     __syncthreads();
-  }
-  const int krow_lane = perm32(lq);
-
-  for (int kt = kt0, it = 0; kt < kt1; ++kt, ++it) {
-    const int buf = it & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) load_kv_tile<D, NT, KCH, VCH>(pk, pv, kg, a.k_sn, vg, a.npad, kt + 1, N, tid);
-    const __bf16* ks = smem + buf * STAGE;
-    const __bf16* vs = ks + KTILE;
-
-    // S^T = K Q^T for the two 32-key blocks of the tile
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const __bf16* kr = ks + (kb * 32 + krow_lane) * KROW + hh * 8;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(kr + kk * 16), qf[kk], s[kb], 0, 0, 0);
-    }
-
-    // bias class of this (wave, key tile)
-    const int kbase = kt * kBlockK;
+    qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
+    if (kt0 + 1 < kt1) load_k_tile<D, NT, KCH>(pk, ktile_base(kt0 + 1), koff, krow, N - (kt0 + 1) * kBlockK, k_sn_bytes);
+    const int kbase = kt0 * kBlockK;
     const bool partial = kbase < k0 || kbase + kBlockK > k1;
-    float brow = 0.0f;
-    bool elem = partial;
-    if (!partial) {
-      const KeyTileSummary sm = ks_b[kt];
-      bool lane_elem = false;
-      if (sm.kind == KT_GUIDE) {
-        if (qbiased) {
-          const float dlo = sm.lo - tq, dhi = tq - sm.hi;
-          const float dmin = fmaxf(fmaxf(dlo, dhi), 0.0f);
-          const float dmax = fmaxf(-dlo, -dhi);
-          if (dmin >= a.dsat) brow = -a.cap2;
-          else if (!(dmax <= a.window)) lane_elem = true;
-        }
-      } else if (sm.kind == KT_PICTURE) {
-        brow = mq * sm.bias;
-      } else if (sm.kind == KT_MIXED) {
-        lane_elem = true;
-      }
-      elem = wave_any(lane_elem);
-    }
+    float brow;
     float cc = a.c;
-    if (elem) {
-      // per-element bias; keys outside [k0, k1) get -inf
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int kx = kbase + kb * 32 + c2 * 16 + hh * 8;
-          const f32x4 t0 = *reinterpret_cast<const f32x4*>(tkb + kx);
-          const f32x4 t1 = *reinterpret_cast<const f32x4*>(tkb + kx + 4);
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(kbb + kx);
-          const f32x4 g1 = *reinterpret_cast<const f32x4*>(kbb + kx + 4);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float tk = e < 4 ? t0[e] : t1[e - 4];
-            const float gk = e < 4 ? g0[e] : g1[e - 4];
-            const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);   // NaN time -> 0
-            const float pen = fminf(dd * dd, a.cap2);
-            float x = fmaf(s[kb][c2 * 8 + e], a.c, fmaf(mq, gk, -pen));
-            if (partial && (kx + e < k0 || kx + e >= k1)) x = -INFINITY;
-            s[kb][c2 * 8 + e] = x;
-          }
-        }
-      }
+    if (tile_class(load_summary(ks_c, kt0), partial, qbiased, tq, mq, a, &brow)) {
+      elem_bias(x, kbase, hh, tq, mq, partial, k0, k1, tkb, kbb, a);
       cc = 1.0f;
+      brow = 0.0f;
     }
-
-    // online softmax (exp2 domain), lazily rescaled
-    float mx = s[0][0];
+    float mx = x[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xor32_max(mx);
-    const float mt = fmaf(mx, cc, brow);
-    const bool grow = mt > m_used + kRescaleTau;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+    m_used = fmaf(xor32_max(mx), cc, brow);
+    const float off = brow - m_used;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(x[kb][r], cc, off);
+    if (kt0 + 1 < kt1) store_tile<KCH>(pk, KBUF(1), ksoff);
+    sm_next = load_summary(ks_c, min(kt0 + 1, kt1 - 1));
+    __syncthreads();
+  }
+
+  for (int t = kt0, j = 0; t < kt1; ++t, ++j) {
+    const bool has1 = t + 1 < kt1, has2 = t + 2 < kt1;
+    if (has2) load_k_tile<D, NT, KCH>(pk, ktile_base(t + 2), koff, krow, N - (t + 2) * kBlockK, k_sn_bytes);
+    if (has1) load_v_tile<VCH>(pv, vtile_base(t + 1), voff);
+    const __bf16* kn = KBUF((j + 1) & 1);
+    const __bf16* vc = VBUF(j & 1);
+    const int kbase1 = (t + 1) * kBlockK;
+    const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
+    const KeyTileSummary sm1 = sm_next;
+
+    // phase A: S_{t+1} = K_{t+1} Q^T (16 MFMAs, the two 32-key blocks
+    // alternating) | P_t = exp2(X_t) in place and its bf16 pack, two elements
+    // per MFMA. K fragments are read from LDS two MFMAs ahead.
+    f32x16 sn[2] = {f32x16{}, f32x16{}};
+    const __bf16* kr0 = kn + krow_lane * KROW + hh * 8;
+    bf16x8 kf[3];
+    kf[0] = kfrag<KROW>(kr0, 0);
+    kf[1] = kfrag<KROW>(kr0, 1);
+    u32x4 pw[4];   // P_t as packed bf16 pairs: pw[kb*2 + c2] is the B operand of PV block (kb, c2)
+#pragma unroll
+    for (int i = 0; i < 2 * NKK; ++i) {
+      if (i + 2 < 2 * NKK) kf[(i + 2) % 3] = kfrag<KROW>(kr0, i + 2);
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
+      if (i < 16) {
+        // elements 2i, 2i+1 of the lane's 32 scores of tile t
+        const int kb = i >> 3, r = (2 * i) & 15;
+        const float p0 = fast_exp2(x[kb][r]), p1 = fast_exp2(x[kb][r + 1]);
+        x[kb][r] = p0;
+        x[kb][r + 1] = p1;
+        pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (2 * NKK < 16) {
+#pragma unroll
+      for (int i = 2 * NKK; i < 16; ++i) {
+        const int kb = i >> 3, r = (2 * i) & 15;
+        const float p0 = fast_exp2(x[kb][r]), p1 = fast_exp2(x[kb][r + 1]);
+        x[kb][r] = p0;
+        x[kb][r + 1] = p1;
+        pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
+      }
+    }
+    // keep P_t in this block (the PV product that reads it follows the
+    // bias-class branch)
+    asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]));
+
+    // bias class of tile t+1 (rare per-element path before phase B)
+    float brow = 0.0f, cc = a.c;
+    if (has1 && tile_class(sm1, partial1, qbiased, tq, mq, a, &brow)) {
+      elem_bias(sn, kbase1, hh, tq, mq, partial1, k0, k1, tkb, kbb, a);
+      cc = 1.0f;
+      brow = 0.0f;
+    }
+
+    // phase B: O^T += V_t^T P_t^T (16 MFMAs over 4 accumulators) | row sum of
+    // P_t, max of S_{t+1}, X_{t+1} = S_{t+1} c + brow - m. V^T fragments are
+    // read two MFMAs ahead.
+    const __bf16* vr0 = vc + lq * VROW + hh * 8;
+    bf16x8 vf[3];
+    vf[0] = vfrag<VROW, NDB>(vr0, 0);
+    vf[1] = vfrag<VROW, NDB>(vr0, 1);
+    float ts0 = 0.0f, ts1 = 0.0f, mxa = -INFINITY, mxb = -INFINITY, mt = 0.0f, off = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4 * NDB; ++i) {
+      if (i + 2 < 4 * NDB) vf[(i + 2) % 3] = vfrag<VROW, NDB>(vr0, i + 2);
+      const int db = i % NDB, kc = i / NDB;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
+      // spread 32 sums, 16 max3 and 32 scale-FMAs over the MFMAs
+      constexpr int NM = 4 * NDB;
+      constexpr int SUMS = (32 + NM - 1) / NM;
+#pragma unroll
+      for (int u = 0; u < SUMS; ++u) {
+        const int f = i * SUMS + u;
+        if (f < 32) {
+          if (f & 1) ts1 += x[f >> 4][f & 15];
+          else ts0 += x[f >> 4][f & 15];
+        }
+      }
+      if (i < NM / 2) {
+        constexpr int MX = (16 + NM / 2 - 1) / (NM / 2);
+#pragma unroll
+        for (int u = 0; u < MX; ++u) {
+          const int f = 2 * (i * MX + u);
+          if (f < 32) {
+            if (u & 1) mxb = max3f(mxb, sn[f >> 4][f & 15], sn[f >> 4][(f & 15) + 1]);
+            else mxa = max3f(mxa, sn[f >> 4][f & 15], sn[f >> 4][(f & 15) + 1]);
+          }
+        }
+        if (i == NM / 2 - 1) {
+          mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow);
+          off = brow - m_used;
+        }
+      } else {
+        constexpr int FM = (32 + NM / 2 - 1) / (NM / 2);
+#pragma unroll
+        for (int u = 0; u < FM; ++u) {
+          const int f = (i - NM / 2) * FM + u;
+          if (f < 32) x[f >> 4][f & 15] = fmaf(sn[f >> 4][f & 15], cc, off);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum += ts0 + ts1;
+    const bool grow = has1 && mt > m_used + kRescaleTau;
     if (wave_any(grow)) {
+      // lazy rescale: move the exponent reference only when a row max grew by > tau
       const float mn = grow ? mt : m_used;
       const float alpha = fast_exp2(m_used - mn);
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) o[i] *= alpha;
       m_used = mn;
+      off = brow - m_used;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(sn[kb][r], cc, off);
     }
-    const float off = brow - m_used;
-    bf16x8 pf[2][2];
-    float tsum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(fmaf(s[kb][c2 * 8 + e], cc, off));
-          tsum += p;
-          pf[kb][c2][e] = (__bf16)p;
-        }
-    lsum += tsum;
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const __bf16* vr = vs + lq * VROW + kb * 32 + c2 * 16 + hh * 8;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *reinterpret_cast<const bf16x8*>(vr + db * 32 * VROW), pf[kb][c2], o[db], 0, 0, 0);
-      }
-
-    if (more)
-      store_kv_tile<D, NT, KCH, VCH, KROW, VROW>(pk, pv, smem + (buf ^ 1) * STAGE,
-                                                 smem + (buf ^ 1) * STAGE + KTILE, tid);
+    if (has2) store_tile<KCH>(pk, KBUF(j & 1), ksoff);
+    if (has1) store_tile<VCH>(pv, VBUF((j + 1) & 1), vsoff);
+    // summary of tile t+2 (scalar load; completes at the barrier's wait)
+    sm_next = load_summary(ks_c, min(t + 2, kt1 - 1));
     __syncthreads();
   }
 
   // epilogue
   const float ltot = xor32_sum(lsum);
   if (!qvalid) return;
-  if (kt0 >= kt1) {
-    if (!PART) return;   // fused calls always have N >= 1 keys
-    // empty partition: contributes nothing to the merge
-    float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
-    if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = -INFINITY;
-    return;
-  }
   const float inv = 1.0f / ltot;
   const float lse = (m_used + __log2f(ltot)) * kLn2;
   if (PART) {
@@ -427,10 +593,10 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f32x4 x;
+        f32x4 y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = o[db][j * 4 + i] * inv;
-        *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = x;
+        for (int i = 0; i < 4; ++i) y[i] = o[db][j * 4 + i] * inv;
+        *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = y;
       }
     if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = lse;
   } else {
@@ -439,16 +605,21 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x4 x;
+        bf16x4 y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (__bf16)(o[db][j * 4 + i] * inv);
-        *reinterpret_cast<bf16x4*>(op + db * 32 + j * 8 + hh * 4) = x;
+        for (int i = 0; i < 4; ++i) y[i] = (__bf16)(o[db][j * 4 + i] * inv);
+        *reinterpret_cast<bf16x4*>(op + db * 32 + j * 8 + hh * 4) = y;
       }
     if (hh == 0) a.lse[((int64_t)b * a.H + h) * N + qrow] = lse;
   }
 }
 
-int attn_bf16_block_q(int) { return kBQ; }
+#undef KBUF
+#undef VBUF
+
+constexpr int kWaves = 8;                 // waves per workgroup of the bf16 kernel
+
+int attn_bf16_block_q(int) { return kWaves * 32; }
 
 int attn_bf16_grid(const AttnArgs& a) { return a.nqb * a.B * a.H; }
 
@@ -456,11 +627,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool partitioned, hipStrea
   dim3 grid(attn_bf16_grid(a), partitioned ? a.nparts : 1);
   dim3 block(kWaves * 64);
   if (D == 128) {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, block, 0, s, a);
+    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, false>), grid, block, 0, s, a);
   } else {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, block, 0, s, a);
+    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
