@@ -34,7 +34,7 @@ bool env_flag(const char* name) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tq, mq, tk, kb, ksum, vt, opart, lsepart, total;
+  size_t tq, mq, tk, kb, ksum, vt, kmax, opart, lsepart, total;
 };
 
 int npad_of(int N) { return (N + tara::kBlockK - 1) / tara::kBlockK * tara::kBlockK; }
@@ -58,6 +58,7 @@ WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tar
   L.kb = take((size_t)B * npad * 4);
   L.ksum = take((size_t)B * nkt * sizeof(tara::KeyTileSummary));
   L.vt = dtype == TARA_BF16 ? take((size_t)B * H * D * npad * 2) : 0;
+  L.kmax = dtype == TARA_BF16 ? take((size_t)B * H * nkt * 4) : 0;
   if (p->mode == TARA_MODE_PARTITIONED) {
     const size_t parts = (size_t)p->num_partitions;
     L.opart = take(parts * B * H * N * D * 4);
@@ -331,6 +332,7 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   aa.tk = ma.tk;
   aa.kb = ma.kb;
   aa.ksum = ma.ksum;
+  aa.kmax = dtype == TARA_BF16 ? reinterpret_cast<const float*>(ws + L.kmax) : nullptr;
   aa.c = (float)(scale * log2e);
   const double sigma = bias_active ? std::sqrt((double)p->strength * log2e) / (double)p->falloff : 0.0;
   aa.sigma = (float)sigma;
@@ -353,6 +355,11 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     e = tara::launch_vtranspose(static_cast<const __bf16*>(v), v_str[0], v_str[1], v_str[2],
                                 const_cast<__bf16*>(aa.vt), B, H, N, npad, D, stream);
     ++launches;
+    if (e == hipSuccess) {
+      e = tara::launch_knorm(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
+                             const_cast<float*>(aa.kmax), B, H, N, nkt, D, stream);
+      ++launches;
+    }
   }
   if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
 

@@ -70,6 +70,7 @@ struct AttnArgs {
   const float* tk;
   const float* kb;
   const KeyTileSummary* ksum;
+  const float* kmax;       // bf16 path: [B*H][nkt] max |k| per key tile
   float c;                 // softmax_scale * log2 e
   float sigma;             // sqrt(strength * log2 e) / falloff  (1/s)
   float w;                 // window * sigma
@@ -92,6 +93,8 @@ struct MergeArgs {
 hipError_t launch_meta(const MetaArgs& a, hipStream_t s);
 hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn, __bf16* vt,
                              int B, int H, int N, int npad, int D, hipStream_t s);
+hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, float* kmax, int B, int H, int N,
+                        int nkt, int D, hipStream_t s);
 // Block of query rows per workgroup of the bf16 attention kernel.
 int attn_bf16_block_q(int D);
 int attn_bf16_grid(const AttnArgs& a);

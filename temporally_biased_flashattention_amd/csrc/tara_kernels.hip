@@ -45,10 +45,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.6931471805599453f;
-// Lazy rescaling threshold (log2 units): the running max used for the
-// exponent is only moved when a row's max grows by more than this, so
-// unnormalised probabilities stay <= 2^8.
-constexpr float kRescaleTau = 8.0f;
+// Lazy rescaling threshold (log2 units): the reference m used in the exponent
+// only moves when a row's logits may exceed it by more than this, so the
+// unnormalised probabilities stay <= 2^20 (far from fp32 / bf16 overflow;
+// relative precision does not depend on the scale).
+constexpr float kRescaleTau = 20.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -178,6 +179,35 @@ hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn
   return hipGetLastError();
 }
 
+// ------------------------------------------------------ key-tile norm bound
+// kmax[b*H + h][t] = max |k_n| over the 64 keys of tile t (rows past N repeat
+// row N-1, as the attention kernel's staging does). One wave per tile.
+__global__ __launch_bounds__(64) void knorm_kernel(const __bf16* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
+                                                   int H, int N, int D, int nkt, float* __restrict__ kmax) {
+  const int t = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int n = min(t * kBlockK + (int)threadIdx.x, N - 1);
+  const __bf16* kp = k + b * sb + h * sh + (int64_t)n * sn;
+  float ss = 0.0f;
+  for (int i = 0; i < D; i += 8) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(kp + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = (float)v[e];
+      ss = fmaf(f, f, ss);
+    }
+  }
+  float r = sqrtf(ss);
+  for (int off = 32; off >= 1; off >>= 1) r = fmaxf(r, __shfl_xor(r, off));
+  if (threadIdx.x == 0) kmax[(int64_t)bh * nkt + t] = r;
+}
+
+hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, float* kmax, int B, int H, int N,
+                        int nkt, int D, hipStream_t s) {
+  dim3 grid(nkt, B * H);
+  hipLaunchKernelGGL(knorm_kernel, grid, dim3(64), 0, s, k, sb, sh, sn, H, N, D, nkt, kmax);
+  return hipGetLastError();
+}
+
 // --------------------------------------------------------- bf16 MFMA kernel
 // One workgroup = NW waves x 32 query rows of one (batch, head). Per 64-key
 // tile t every wave runs a two-phase software pipeline so that its MFMAs and
@@ -188,35 +218,82 @@ hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn
 // so K runs one tile ahead of V in LDS: iteration t reads K_{t+1} and V_t and
 // stages K_{t+2} and V_{t+1} (two LDS buffers each, one barrier per tile).
 
+// LDS ring depth of the bf16 kernel (K/V^T tile pairs in flight).
+constexpr int kStages = 4;
+
 // Key row held by S^T output row `r` of a 32-key block: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-template <int D, int NT, int KCH>
-__device__ __forceinline__ void load_k_tile(u32x4 (&pk)[KCH], const char* kg_tile, const uint32_t (&koff)[KCH],
-                                            const int (&krow)[KCH], int rows_left, int64_t k_sn_bytes) {
-  // rows beyond the sequence (tail tile) re-read its last row; their keys are masked
-  if (rows_left >= kBlockK) {
+__device__ __forceinline__ void dma16(const char* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Tile staging by LDS DMA (global_load_lds_dwordx4): one wave instruction
+// writes 64 lanes x 16 bytes contiguously at a uniform LDS address. Every call
+// stages one padded K tile (64 rows of KROW elements) and one padded V^T tile
+// (D rows of VROW) as whole 1-KB blocks: combined block ci < KBLK is K, the
+// rest V^T, and wave w takes blocks w, w + NW, .... Every wave issues exactly
+// PER_WAVE DMAs per call (a wave with fewer blocks repeats its first block,
+// which rewrites the same bytes), so the issue is branch-free and the count of
+// pending DMAs is the same in every wave. A lane whose 16 bytes fall on a
+// row's pad chunk re-reads chunk 0 of its row (never read back).
+template <int KROWB, int KDATA, int KBLK, int VROWB, int VDATA, int VBLK, int NW>
+struct KvDma {
+  static constexpr int TOT = KBLK + VBLK;
+  static constexpr int PER_WAVE = (TOT + NW - 1) / NW;
+  uint32_t goff[PER_WAVE];   // byte offset of this lane's 16 bytes in its global tile
+  int krow[PER_WAVE];        // K tile row of those bytes (for the tail clamp); -1 for V^T
+  __device__ void init(int wave, int lane, int64_t k_row_bytes, int64_t v_row_bytes) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) pk[i] = *reinterpret_cast<const u32x4*>(kg_tile + koff[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int extra = krow[i] - min(krow[i], rows_left - 1);
-      pk[i] = *reinterpret_cast<const u32x4*>(kg_tile + koff[i] - (int64_t)extra * k_sn_bytes);
+    for (int p = 0; p < PER_WAVE; ++p) {
+      const int ci = block(wave, p);
+      if (ci < KBLK) {
+        const int o = ci * 1024 + lane * 16, r = o / KROWB, c = (o % KROWB) / 16;
+        krow[p] = r;
+        goff[p] = (uint32_t)(r * k_row_bytes + (c < KDATA ? c * 16 : 0));
+      } else {
+        const int o = (ci - KBLK) * 1024 + lane * 16, d = o / VROWB, c = (o % VROWB) / 16;
+        krow[p] = -1;
+        goff[p] = (uint32_t)(d * v_row_bytes + (c < VDATA ? c * 16 : 0));
+      }
     }
   }
-}
-
-template <int VCH>
-__device__ __forceinline__ void load_v_tile(u32x4 (&pv)[VCH], const char* vg_tile, const uint32_t (&voff)[VCH]) {
+  // combined block index of this wave's p-th DMA (uniform)
+  __device__ static int block(int wave, int p) {
+    const int ci = wave + p * NW;
+    return ci < TOT ? ci : wave;
+  }
+  // K rows past the sequence (tail tile) re-read its last row; those keys are masked later.
+  __device__ void issue(const char* kg_tile, int rows_left, int64_t k_row_bytes, char* lds_k, const char* vg_tile,
+                        char* lds_v, int wave) const {
+    if (rows_left >= kBlockK) {
 #pragma unroll
-  for (int i = 0; i < VCH; ++i) pv[i] = *reinterpret_cast<const u32x4*>(vg_tile + voff[i]);
-}
-
-template <int N>
-__device__ __forceinline__ void store_tile(const u32x4 (&p)[N], __bf16* lds, const uint32_t (&soff)[N]) {
+      for (int p = 0; p < PER_WAVE; ++p) {
+        const int ci = block(wave, p);
+        const bool isk = ci < KBLK;
+        const char* g = isk ? kg_tile : vg_tile;
+        char* l = isk ? lds_k + ci * 1024 : lds_v + (ci - KBLK) * 1024;
+        dma16(g + goff[p], l);
+      }
+    } else {
 #pragma unroll
-  for (int i = 0; i < N; ++i) *reinterpret_cast<u32x4*>(lds + soff[i]) = p[i];
+      for (int p = 0; p < PER_WAVE; ++p) {
+        const int ci = block(wave, p);
+        const bool isk = ci < KBLK;
+        const char* g = isk ? kg_tile - (int64_t)(krow[p] - min(krow[p], rows_left - 1)) * k_row_bytes : vg_tile;
+        char* l = isk ? lds_k + ci * 1024 : lds_v + (ci - KBLK) * 1024;
+        dma16(g + goff[p], l);
+      }
+    }
+  }
+};
+
+// Wait until at most KEEP of this wave's vector-memory operations are pending
+// (the newest KEEP DMAs may stay in flight).
+template <int KEEP>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KEEP) : "memory");
 }
 
 // S^T for the two 32-key blocks of a K tile in LDS.
@@ -339,15 +416,13 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int VROW = kBlockK + 8;        // padded LDS pitch of a V^T row (elements)
   constexpr int KTILE = kBlockK * KROW;
   constexpr int VTILE = D * VROW;
-  constexpr int KCH = kBlockK * D / 8 / NT;   // 16-byte chunks per thread, K tile
-  constexpr int VCH = D * kBlockK / 8 / NT;   // 16-byte chunks per thread, V^T tile
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  static_assert(KCH * NT * 8 == kBlockK * D && VCH * NT * 8 == kBlockK * D, "tile split");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * KTILE + 2 * VTILE];
-  // LDS: K buffers 0/1 then V^T buffers 0/1
+  // LDS ring of NS stages: K tiles in slots 0..NS-1, then V^T tiles in slots 0..NS-1
+  constexpr int NS = kStages;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[NS * (KTILE + VTILE)];
 #define KBUF(i) (smem + (i) * KTILE)
-#define VBUF(i) (smem + 2 * KTILE + (i) * VTILE)
+#define VBUF(i) (smem + NS * KTILE + (i) * VTILE)
 
   const int part = PART ? blockIdx.y : 0;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -355,7 +430,8 @@ void attn_bf16_kernel(AttnArgs a) {
   const int b = bh / a.H, h = bh % a.H;
   const int N = a.N;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int qrow = qblk * BQ + wave * 32 + lq;
   const bool qvalid = qrow < N;
   const int qr = qvalid ? qrow : N - 1;
@@ -383,27 +459,27 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   const int kt0 = k0 / kBlockK, kt1 = (k1 + kBlockK - 1) / kBlockK;
 
-  // staging addresses: 32-bit byte offsets from a per-tile scalar base
+  // staging: 32-bit byte offsets from a per-tile scalar base
   const char* kg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh);
   const char* vg = reinterpret_cast<const char*>(a.vt + (int64_t)bh * D * a.npad);
   const int64_t k_sn_bytes = a.k_sn * 2;
-  uint32_t koff[KCH], ksoff[KCH], voff[VCH], vsoff[VCH];
-  int krow[KCH];
-#pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int c = tid + i * NT, r = c / (D / 8), c8 = c % (D / 8);
-    krow[i] = r;
-    koff[i] = (uint32_t)(r * k_sn_bytes + c8 * 16);
-    ksoff[i] = r * KROW + c8 * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < VCH; ++i) {
-    const int c = tid + i * NT, d = c / (kBlockK / 8), c8 = c % (kBlockK / 8);
-    voff[i] = (uint32_t)((d * a.npad + c8 * 8) * 2);
-    vsoff[i] = d * VROW + c8 * 8;
-  }
+  constexpr int KBLK = KTILE * 2 / 1024, VBLK = VTILE * 2 / 1024;
+  static_assert(KBLK * 1024 == KTILE * 2 && VBLK * 1024 == VTILE * 2, "tiles are whole 1-KB blocks");
   auto ktile_base = [&](int kt) { return kg + (int64_t)kt * kBlockK * k_sn_bytes; };
   auto vtile_base = [&](int kt) { return vg + (int64_t)kt * kBlockK * 2; };
+  using Dma = KvDma<KROW * 2, D / 8, KBLK, VROW * 2, kBlockK / 8, VBLK, NW>;
+  Dma dma;
+  dma.init(wave, lane, k_sn_bytes, (int64_t)a.npad * 2);
+  // stage K tile kk into K slot sk and V^T tile kv into V slot sv (indices past
+  // the range are clamped to its last tile: the slot is free either way)
+  auto stage = [&](int kk, int sk, int kv, int sv) {
+    kk = min(kk, kt1 - 1);
+    kv = min(kv, kt1 - 1);
+    dma.issue(ktile_base(kk), N - kk * kBlockK, k_sn_bytes, reinterpret_cast<char*>(KBUF(sk)), vtile_base(kv),
+              reinterpret_cast<char*>(VBUF(sv)), wave);
+  };
+  // keep this iteration's DMAs (and those of the NS-3 before it) in flight
+  auto wait_staged = [&]() { wait_vm<(NS - 2) * Dma::PER_WAVE>(); };
 
   const float* tkb = a.tk + (int64_t)b * a.npad;
   const float* kbb = a.kb + (int64_t)b * a.npad;
@@ -413,23 +489,37 @@ void attn_bf16_kernel(AttnArgs a) {
   const KsumConstPtr ks_c = (KsumConstPtr)ks_b;
   const int krow_lane = perm32(lq);
   KeyTileSummary sm_next;
+  // max over each key tile of |k| (this head), for the row-max bound
+  const __attribute__((address_space(4))) float* kmax_c =
+      (const __attribute__((address_space(4))) float*)(a.kmax + (int64_t)bh * a.nkt);
+  float kmax_next;
+  // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum
+  float qn_c;
+  {
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (float)qf[kk][e];
+        ss = fmaf(v, v, ss);
+      }
+    qn_c = sqrtf(xor32_sum(ss)) * a.c * (1.0f + 0x1.0p-10f);
+  }
 
   f32x16 o[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m_used = -INFINITY, lsum = 0.0f;
   f32x16 x[2];   // X_t = S_t * c + bias - m_used (exp2 argument)
-  u32x4 pk[KCH], pv[VCH];
 
   {
-    // prologue: K_t0, V_t0 staged; S_t0; X_t0; K_{t0+1} staged
-    load_k_tile<D, NT, KCH>(pk, ktile_base(kt0), koff, krow, N - kt0 * kBlockK, k_sn_bytes);
-    load_v_tile<VCH>(pv, vtile_base(kt0), voff);
-    store_tile<KCH>(pk, KBUF(0), ksoff);
-    store_tile<VCH>(pv, VBUF(0), vsoff);
-    __syncthreads();
+    // prologue: K and V^T of tiles t0 .. t0+NS-1 into slots 0 .. NS-1; S_t0; X_t0
+#pragma unroll
+    for (int i = 0; i < NS; ++i) stage(kt0 + i, i, kt0 + i, i);
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
     qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
-    if (kt0 + 1 < kt1) load_k_tile<D, NT, KCH>(pk, ktile_base(kt0 + 1), koff, krow, N - (kt0 + 1) * kBlockK, k_sn_bytes);
     const int kbase = kt0 * kBlockK;
     const bool partial = kbase < k0 || kbase + kBlockK > k1;
     float brow;
@@ -450,34 +540,42 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(x[kb][r], cc, off);
-    if (kt0 + 1 < kt1) store_tile<KCH>(pk, KBUF(1), ksoff);
     sm_next = load_summary(ks_c, min(kt0 + 1, kt1 - 1));
-    __syncthreads();
+    kmax_next = kmax_c[min(kt0 + 1, kt1 - 1)];
+    // every wave is done with K slot 0 before iteration 0 restages it
+    __builtin_amdgcn_s_barrier();
   }
 
-  for (int t = kt0, j = 0; t < kt1; ++t, ++j) {
-    const bool has1 = t + 1 < kt1, has2 = t + 2 < kt1;
-    if (has2) load_k_tile<D, NT, KCH>(pk, ktile_base(t + 2), koff, krow, N - (t + 2) * kBlockK, k_sn_bytes);
-    if (has1) load_v_tile<VCH>(pv, vtile_base(t + 1), voff);
-    const __bf16* kn = KBUF((j + 1) & 1);
-    const __bf16* vc = VBUF(j & 1);
+  // ring slots: iteration j reads K_{t+1} (slot s1) and V_t (slot s0), and
+  // restages K_{t+NS} into slot s0 (K_t's, read last iteration) and
+  // V_{t+NS-1} into slot sprev (V_{t-1}'s, read last iteration)
+  int s0 = 0;
+  for (int t = kt0; t < kt1; ++t) {
+    const bool has1 = t + 1 < kt1;
+    const int s1 = s0 + 1 == NS ? 0 : s0 + 1;
+    const int sprev = s0 == 0 ? NS - 1 : s0 - 1;
+    stage(t + NS, s0, t + NS - 1, sprev);
+    const __bf16* kn = KBUF(s1);
+    const __bf16* vc = VBUF(s0);
     const int kbase1 = (t + 1) * kBlockK;
     const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
     const KeyTileSummary sm1 = sm_next;
+    const float kmax1 = kmax_next;
 
     // phase A: S_{t+1} = K_{t+1} Q^T (16 MFMAs, the two 32-key blocks
     // alternating) | P_t = exp2(X_t) in place and its bf16 pack, two elements
-    // per MFMA. K fragments are read from LDS two MFMAs ahead.
+    // per MFMA. K fragments are read from LDS three MFMAs ahead.
     f32x16 sn[2] = {f32x16{}, f32x16{}};
     const __bf16* kr0 = kn + krow_lane * KROW + hh * 8;
-    bf16x8 kf[3];
+    bf16x8 kf[4];
     kf[0] = kfrag<KROW>(kr0, 0);
     kf[1] = kfrag<KROW>(kr0, 1);
+    kf[2] = kfrag<KROW>(kr0, 2);
     u32x4 pw[4];   // P_t as packed bf16 pairs: pw[kb*2 + c2] is the B operand of PV block (kb, c2)
 #pragma unroll
     for (int i = 0; i < 2 * NKK; ++i) {
-      if (i + 2 < 2 * NKK) kf[(i + 2) % 3] = kfrag<KROW>(kr0, i + 2);
-      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
+      if (i + 3 < 2 * NKK) kf[(i + 3) & 3] = kfrag<KROW>(kr0, i + 3);
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
       if (i < 16) {
         // elements 2i, 2i+1 of the lane's 32 scores of tile t
         const int kb = i >> 3, r = (2 * i) & 15;
@@ -504,83 +602,79 @@ void attn_bf16_kernel(AttnArgs a) {
 
     // bias class of tile t+1 (rare per-element path before phase B)
     float brow = 0.0f, cc = a.c;
-    if (has1 && tile_class(sm1, partial1, qbiased, tq, mq, a, &brow)) {
-      elem_bias(sn, kbase1, hh, tq, mq, partial1, k0, k1, tkb, kbb, a);
-      cc = 1.0f;
-      brow = 0.0f;
+    bool need_max = false;
+    if (has1) {
+      if (tile_class(sm1, partial1, qbiased, tq, mq, a, &brow)) {
+        elem_bias(sn, kbase1, hh, tq, mq, partial1, k0, k1, tkb, kbb, a);
+        cc = 1.0f;
+        brow = 0.0f;
+        need_max = true;
+      } else {
+        // every logit of the tile is <= |q| max|k| c + brow (Cauchy-Schwarz);
+        // the exact row max is needed only when that bound could pass m + tau
+        need_max = wave_any(fmaf(qn_c, kmax1, brow) > m_used + kRescaleTau);
+      }
     }
+    float m_new = m_used;
+    if (need_max) {
+      float mxa = -INFINITY, mxb = -INFINITY;
+#pragma unroll
+      for (int f = 0; f < 32; f += 4) {
+        mxa = max3f(mxa, sn[f >> 4][f & 15], sn[f >> 4][(f & 15) + 1]);
+        mxb = max3f(mxb, sn[f >> 4][(f & 15) + 2], sn[f >> 4][(f & 15) + 3]);
+      }
+      const float mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow);
+      if (mt > m_used + kRescaleTau) m_new = mt;
+    }
+    const float off = brow - m_new;
 
     // phase B: O^T += V_t^T P_t^T (16 MFMAs over 4 accumulators) | row sum of
-    // P_t, max of S_{t+1}, X_{t+1} = S_{t+1} c + brow - m. V^T fragments are
-    // read two MFMAs ahead.
+    // P_t, X_{t+1} = S_{t+1} c + brow - m_new. V^T fragments are read three
+    // MFMAs ahead.
     const __bf16* vr0 = vc + lq * VROW + hh * 8;
-    bf16x8 vf[3];
+    bf16x8 vf[4];
     vf[0] = vfrag<VROW, NDB>(vr0, 0);
     vf[1] = vfrag<VROW, NDB>(vr0, 1);
-    float ts0 = 0.0f, ts1 = 0.0f, mxa = -INFINITY, mxb = -INFINITY, mt = 0.0f, off = 0.0f;
+    vf[2] = vfrag<VROW, NDB>(vr0, 2);
+    float ts0 = 0.0f, ts1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4 * NDB; ++i) {
-      if (i + 2 < 4 * NDB) vf[(i + 2) % 3] = vfrag<VROW, NDB>(vr0, i + 2);
+      if (i + 3 < 4 * NDB) vf[(i + 3) & 3] = vfrag<VROW, NDB>(vr0, i + 3);
       const int db = i % NDB, kc = i / NDB;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
-      // spread 32 sums, 16 max3 and 32 scale-FMAs over the MFMAs
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
+      // spread 32 sums and 32 scale-FMAs over the MFMAs
       constexpr int NM = 4 * NDB;
-      constexpr int SUMS = (32 + NM - 1) / NM;
+      constexpr int PER = (32 + NM - 1) / NM;
 #pragma unroll
-      for (int u = 0; u < SUMS; ++u) {
-        const int f = i * SUMS + u;
+      for (int u = 0; u < PER; ++u) {
+        const int f = i * PER + u;
         if (f < 32) {
           if (f & 1) ts1 += x[f >> 4][f & 15];
           else ts0 += x[f >> 4][f & 15];
-        }
-      }
-      if (i < NM / 2) {
-        constexpr int MX = (16 + NM / 2 - 1) / (NM / 2);
-#pragma unroll
-        for (int u = 0; u < MX; ++u) {
-          const int f = 2 * (i * MX + u);
-          if (f < 32) {
-            if (u & 1) mxb = max3f(mxb, sn[f >> 4][f & 15], sn[f >> 4][(f & 15) + 1]);
-            else mxa = max3f(mxa, sn[f >> 4][f & 15], sn[f >> 4][(f & 15) + 1]);
-          }
-        }
-        if (i == NM / 2 - 1) {
-          mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow);
-          off = brow - m_used;
-        }
-      } else {
-        constexpr int FM = (32 + NM / 2 - 1) / (NM / 2);
-#pragma unroll
-        for (int u = 0; u < FM; ++u) {
-          const int f = (i - NM / 2) * FM + u;
-          if (f < 32) x[f >> 4][f & 15] = fmaf(sn[f >> 4][f & 15], cc, off);
+          x[f >> 4][f & 15] = fmaf(sn[f >> 4][f & 15], cc, off);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     lsum += ts0 + ts1;
-    const bool grow = has1 && mt > m_used + kRescaleTau;
-    if (wave_any(grow)) {
-      // lazy rescale: move the exponent reference only when a row max grew by > tau
-      const float mn = grow ? mt : m_used;
-      const float alpha = fast_exp2(m_used - mn);
+    if (wave_any(m_new > m_used)) {
+      // lazy rescale after the PV product of tile t (which used the old m)
+      const float alpha = fast_exp2(m_used - m_new);
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) o[i] *= alpha;
-      m_used = mn;
-      off = brow - m_used;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(sn[kb][r], cc, off);
+      m_used = m_new;
     }
 
-    if (has2) store_tile<KCH>(pk, KBUF(j & 1), ksoff);
-    if (has1) store_tile<VCH>(pv, VBUF((j + 1) & 1), vsoff);
-    // summary of tile t+2 (scalar load; completes at the barrier's wait)
+    // K_{t+2} and V_{t+1} (staged NS-2 iterations ago) have landed; newer DMAs may fly on
+    wait_staged();
     sm_next = load_summary(ks_c, min(t + 2, kt1 - 1));
-    __syncthreads();
+    kmax_next = kmax_c[min(t + 2, kt1 - 1)];
+    __builtin_amdgcn_s_barrier();
+    s0 = s1;
   }
+  // no DMA may still target this workgroup's LDS when it exits
+  wait_vm<0>();
 
   // epilogue
   const float ltot = xor32_sum(lsum);

@@ -52,11 +52,12 @@ def test_workspace_bytes():
     npad = 1024
     nkt = npad // 64
     meta = 2 * _al(B * N * 4) + 2 * _al(B * npad * 4) + _al(B * nkt * 16)
-    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p) == meta + _al(B * H * D * npad * 2)
+    bf16_extra = _al(B * H * D * npad * 2) + _al(B * H * nkt * 4)     # V^T, per-tile max |k|
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p) == meta + bf16_extra
     assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, p) == meta
     pp = tara.make_params(mode="partitioned", partitions=3)
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, pp) == (
-        meta + _al(B * H * D * npad * 2) + _al(3 * B * H * N * D * 4) + _al(3 * B * H * N * 4))
+        meta + bf16_extra + _al(3 * B * H * N * D * 4) + _al(3 * B * H * N * 4))
     assert tara.tara_workspace_bytes(tara.TARA_BF16, 0, H, N, D, p) == 0
     with pytest.raises(tara.TaraError):
         tara.tara_workspace_bytes(tara.TARA_BF16, 1, 1, 10, 96, p)
