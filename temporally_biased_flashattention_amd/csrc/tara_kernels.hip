@@ -219,7 +219,7 @@ hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, flo
 // stages K_{t+2} and V_{t+1} (two LDS buffers each, one barrier per tile).
 
 // LDS ring depth of the bf16 kernel (K/V^T tile pairs in flight).
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 
 // Key row held by S^T output row `r` of a 32-key block: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -354,10 +354,11 @@ __device__ __forceinline__ KeyTileSummary load_summary(KsumConstPtr p, int i) {
   return r;
 }
 
-// Bias class of one key tile for this wave: returns true when the tile needs
-// the per-element formula; otherwise *brow is the lane's constant bias (log2).
-__device__ __forceinline__ bool tile_class(const KeyTileSummary& sm, bool partial, bool qbiased, float tq, float mq,
-                                           const AttnArgs& a, float* brow) {
+// Bias class of one key tile for one query row: returns true when the tile
+// needs the per-element formula for this row; otherwise *brow is the row's
+// constant bias over the tile (log2 units).
+__device__ __forceinline__ bool tile_class_lane(const KeyTileSummary& sm, bool partial, bool qbiased, float tq,
+                                                float mq, const AttnArgs& a, float* brow) {
   float b = 0.0f;
   bool lane_elem = partial;
   if (!partial) {
@@ -376,7 +377,7 @@ __device__ __forceinline__ bool tile_class(const KeyTileSummary& sm, bool partia
     }
   }
   *brow = b;
-  return wave_any(lane_elem);
+  return lane_elem;
 }
 
 // Per-element bias of a key tile, in place: x = s*c + m*log2(gain) - penalty,
@@ -407,11 +408,10 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
   }
 }
 
-template <int D, int NW, bool PART>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int NW, int QB, bool PART>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BQ = NW * 32;
+  constexpr int BQ = NW * QB * 32;         // query rows per workgroup
   constexpr int KROW = D + 8;              // padded LDS pitch of a K row (elements)
   constexpr int VROW = kBlockK + 8;        // padded LDS pitch of a V^T row (elements)
   constexpr int KTILE = kBlockK * KROW;
@@ -432,28 +432,40 @@ void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int qrow = qblk * BQ + wave * 32 + lq;
-  const bool qvalid = qrow < N;
-  const int qr = qvalid ? qrow : N - 1;
 
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)qr * a.q_sn;
-  bf16x8 qf[NKK];
+  // this lane's query rows: block q of the wave holds rows wave*32*QB + 32*q + lq
+  int qrow[QB];
+  bool qvalid[QB];
+  bf16x8 qf[QB][NKK];
+  float tq[QB], mq[QB];
+  bool qbiased[QB];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
-  const float tq = a.tq[(int64_t)b * N + qr];
-  const float mq = a.mq[(int64_t)b * N + qr];
-  const bool qbiased = tq == tq;
+  for (int q = 0; q < QB; ++q) {
+    qrow[q] = qblk * BQ + (wave * QB + q) * 32 + lq;
+    qvalid[q] = qrow[q] < N;
+    const int qr = qvalid[q] ? qrow[q] : N - 1;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)qr * a.q_sn;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[q][kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
+    tq[q] = a.tq[(int64_t)b * N + qr];
+    mq[q] = a.mq[(int64_t)b * N + qr];
+    qbiased[q] = tq[q] == tq[q];
+  }
 
   const int k0 = a.kr[part], k1 = a.kr[part + 1];
   if (k1 <= k0) {
     // empty key range (partitioned mode only): contributes nothing to the merge
-    if (PART && qvalid) {
-      float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
+    if (PART) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int q = 0; q < QB; ++q) {
+        if (!qvalid[q]) continue;
+        float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]) * D;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
-      if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = -INFINITY;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
+        if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]] = -INFINITY;
+      }
     }
     return;
   }
@@ -494,24 +506,32 @@ void attn_bf16_kernel(AttnArgs a) {
       (const __attribute__((address_space(4))) float*)(a.kmax + (int64_t)bh * a.nkt);
   float kmax_next;
   // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum
-  float qn_c;
-  {
+  float qn_c[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
     float ss = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = (float)qf[kk][e];
+        const float v = (float)qf[q][kk][e];
         ss = fmaf(v, v, ss);
       }
-    qn_c = sqrtf(xor32_sum(ss)) * a.c * (1.0f + 0x1.0p-10f);
+    qn_c[q] = sqrtf(xor32_sum(ss)) * a.c * (1.0f + 0x1.0p-10f);
   }
 
-  f32x16 o[NDB];
+  f32x16 o[QB][NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
-  float m_used = -INFINITY, lsum = 0.0f;
-  f32x16 x[2];   // X_t = S_t * c + bias - m_used (exp2 argument)
+  for (int q = 0; q < QB; ++q)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[q][i] = f32x16{};
+  float m_used[QB], lsum[QB];
+  f32x16 x[QB][2];   // X_t = S_t * c + bias - m_used (exp2 argument)
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    m_used[q] = -INFINITY;
+    lsum[q] = 0.0f;
+  }
 
   {
     // prologue: K and V^T of tiles t0 .. t0+NS-1 into slots 0 .. NS-1; S_t0; X_t0
@@ -519,34 +539,45 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < NS; ++i) stage(kt0 + i, i, kt0 + i, i);
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) qk_tile<D, KROW>(x[q], KBUF(0), krow_lane, hh, qf[q]);
     const int kbase = kt0 * kBlockK;
     const bool partial = kbase < k0 || kbase + kBlockK > k1;
-    float brow;
+    const KeyTileSummary sm0 = load_summary(ks_c, kt0);
+    float brow[QB];
+    bool lane_elem = false;
+#pragma unroll
+    for (int q = 0; q < QB; ++q) lane_elem |= tile_class_lane(sm0, partial, qbiased[q], tq[q], mq[q], a, &brow[q]);
     float cc = a.c;
-    if (tile_class(load_summary(ks_c, kt0), partial, qbiased, tq, mq, a, &brow)) {
-      elem_bias(x, kbase, hh, tq, mq, partial, k0, k1, tkb, kbb, a);
+    if (wave_any(lane_elem)) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        elem_bias(x[q], kbase, hh, tq[q], mq[q], partial, k0, k1, tkb, kbb, a);
+        brow[q] = 0.0f;
+      }
       cc = 1.0f;
-      brow = 0.0f;
     }
-    float mx = x[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int q = 0; q < QB; ++q) {
+      float mx = x[q][0][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
-    m_used = fmaf(xor32_max(mx), cc, brow);
-    const float off = brow - m_used;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[q][kb][r]);
+      m_used[q] = fmaf(xor32_max(mx), cc, brow[q]);
+      const float off = brow[q] - m_used[q];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(x[kb][r], cc, off);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[q][kb][r] = fmaf(x[q][kb][r], cc, off);
+    }
     sm_next = load_summary(ks_c, min(kt0 + 1, kt1 - 1));
     kmax_next = kmax_c[min(kt0 + 1, kt1 - 1)];
     // every wave is done with K slot 0 before iteration 0 restages it
     __builtin_amdgcn_s_barrier();
   }
 
-  // ring slots: iteration j reads K_{t+1} (slot s1) and V_t (slot s0), and
+  // ring slots: iteration t reads K_{t+1} (slot s1) and V_t (slot s0), and
   // restages K_{t+NS} into slot s0 (K_t's, read last iteration) and
   // V_{t+NS-1} into slot sprev (V_{t-1}'s, read last iteration)
   int s0 = 0;
@@ -562,108 +593,144 @@ void attn_bf16_kernel(AttnArgs a) {
     const KeyTileSummary sm1 = sm_next;
     const float kmax1 = kmax_next;
 
-    // phase A: S_{t+1} = K_{t+1} Q^T (16 MFMAs, the two 32-key blocks
-    // alternating) | P_t = exp2(X_t) in place and its bf16 pack, two elements
-    // per MFMA. K fragments are read from LDS three MFMAs ahead.
-    f32x16 sn[2] = {f32x16{}, f32x16{}};
+    // phase A: S_{t+1} = K_{t+1} Q^T (each K fragment feeds the QB query
+    // blocks; the two 32-key blocks alternate) | P_t = exp2(X_t) in place and
+    // its bf16 pack. K fragments are read from LDS three fragments ahead.
+    f32x16 sn[QB][2];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) sn[q][0] = sn[q][1] = f32x16{};
     const __bf16* kr0 = kn + krow_lane * KROW + hh * 8;
     bf16x8 kf[4];
     kf[0] = kfrag<KROW>(kr0, 0);
     kf[1] = kfrag<KROW>(kr0, 1);
     kf[2] = kfrag<KROW>(kr0, 2);
-    u32x4 pw[4];   // P_t as packed bf16 pairs: pw[kb*2 + c2] is the B operand of PV block (kb, c2)
+    u32x4 pw[QB][4];   // P_t as packed bf16 pairs: pw[q][kb*2 + c2] is the B operand of PV block (kb, c2)
+    auto exp_pair = [&](int q, int i) {
+      // elements 2i, 2i+1 of the lane's 32 scores of tile t (query block q)
+      const int kb = i >> 3, r = (2 * i) & 15;
+      const float p0 = fast_exp2(x[q][kb][r]), p1 = fast_exp2(x[q][kb][r + 1]);
+      x[q][kb][r] = p0;
+      x[q][kb][r + 1] = p1;
+      pw[q][i >> 2][i & 3] = pack_bf16x2(p0, p1);
+    };
 #pragma unroll
     for (int i = 0; i < 2 * NKK; ++i) {
       if (i + 3 < 2 * NKK) kf[(i + 3) & 3] = kfrag<KROW>(kr0, i + 3);
-      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+        sn[q][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[q][i >> 1], sn[q][i & 1], 0, 0, 0);
       if (i < 16) {
-        // elements 2i, 2i+1 of the lane's 32 scores of tile t
-        const int kb = i >> 3, r = (2 * i) & 15;
-        const float p0 = fast_exp2(x[kb][r]), p1 = fast_exp2(x[kb][r + 1]);
-        x[kb][r] = p0;
-        x[kb][r + 1] = p1;
-        pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
+#pragma unroll
+        for (int q = 0; q < QB; ++q) exp_pair(q, i);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (2 * NKK < 16) {
 #pragma unroll
-      for (int i = 2 * NKK; i < 16; ++i) {
-        const int kb = i >> 3, r = (2 * i) & 15;
-        const float p0 = fast_exp2(x[kb][r]), p1 = fast_exp2(x[kb][r + 1]);
-        x[kb][r] = p0;
-        x[kb][r + 1] = p1;
-        pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
-      }
-    }
+    for (int i = 2 * NKK; i < 16; ++i)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) exp_pair(q, i);
     // keep P_t in this block (the PV product that reads it follows the
     // bias-class branch)
-    asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]));
+#pragma unroll
+    for (int q = 0; q < QB; ++q) asm volatile("" ::"v"(pw[q][0]), "v"(pw[q][1]), "v"(pw[q][2]), "v"(pw[q][3]));
 
     // bias class of tile t+1 (rare per-element path before phase B)
-    float brow = 0.0f, cc = a.c;
+    float brow[QB];
+    float cc = a.c;
     bool need_max = false;
+#pragma unroll
+    for (int q = 0; q < QB; ++q) brow[q] = 0.0f;
     if (has1) {
-      if (tile_class(sm1, partial1, qbiased, tq, mq, a, &brow)) {
-        elem_bias(sn, kbase1, hh, tq, mq, partial1, k0, k1, tkb, kbb, a);
+      bool lane_elem = false;
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+        lane_elem |= tile_class_lane(sm1, partial1, qbiased[q], tq[q], mq[q], a, &brow[q]);
+      if (wave_any(lane_elem)) {
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          elem_bias(sn[q], kbase1, hh, tq[q], mq[q], partial1, k0, k1, tkb, kbb, a);
+          brow[q] = 0.0f;
+        }
         cc = 1.0f;
-        brow = 0.0f;
         need_max = true;
       } else {
         // every logit of the tile is <= |q| max|k| c + brow (Cauchy-Schwarz);
         // the exact row max is needed only when that bound could pass m + tau
-        need_max = wave_any(fmaf(qn_c, kmax1, brow) > m_used + kRescaleTau);
-      }
-    }
-    float m_new = m_used;
-    if (need_max) {
-      float mxa = -INFINITY, mxb = -INFINITY;
+        bool lane_need = false;
 #pragma unroll
-      for (int f = 0; f < 32; f += 4) {
-        mxa = max3f(mxa, sn[f >> 4][f & 15], sn[f >> 4][(f & 15) + 1]);
-        mxb = max3f(mxb, sn[f >> 4][(f & 15) + 2], sn[f >> 4][(f & 15) + 3]);
+        for (int q = 0; q < QB; ++q) lane_need |= fmaf(qn_c[q], kmax1, brow[q]) > m_used[q] + kRescaleTau;
+        need_max = wave_any(lane_need);
       }
-      const float mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow);
-      if (mt > m_used + kRescaleTau) m_new = mt;
     }
-    const float off = brow - m_new;
+    float m_new[QB], off[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) m_new[q] = m_used[q];
+    if (need_max) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        float mxa = -INFINITY, mxb = -INFINITY;
+#pragma unroll
+        for (int f = 0; f < 32; f += 4) {
+          mxa = max3f(mxa, sn[q][f >> 4][f & 15], sn[q][f >> 4][(f & 15) + 1]);
+          mxb = max3f(mxb, sn[q][f >> 4][(f & 15) + 2], sn[q][f >> 4][(f & 15) + 3]);
+        }
+        const float mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow[q]);
+        if (mt > m_used[q] + kRescaleTau) m_new[q] = mt;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) off[q] = brow[q] - m_new[q];
 
-    // phase B: O^T += V_t^T P_t^T (16 MFMAs over 4 accumulators) | row sum of
-    // P_t, X_{t+1} = S_{t+1} c + brow - m_new. V^T fragments are read three
-    // MFMAs ahead.
+    // phase B: O^T += V_t^T P_t^T (each V^T fragment feeds the QB query
+    // blocks) | row sum of P_t, X_{t+1} = S_{t+1} c + brow - m_new. V^T
+    // fragments are read three fragments ahead.
     const __bf16* vr0 = vc + lq * VROW + hh * 8;
     bf16x8 vf[4];
     vf[0] = vfrag<VROW, NDB>(vr0, 0);
     vf[1] = vfrag<VROW, NDB>(vr0, 1);
     vf[2] = vfrag<VROW, NDB>(vr0, 2);
-    float ts0 = 0.0f, ts1 = 0.0f;
+    float ts[QB][2];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) ts[q][0] = ts[q][1] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4 * NDB; ++i) {
       if (i + 3 < 4 * NDB) vf[(i + 3) & 3] = vfrag<VROW, NDB>(vr0, i + 3);
       const int db = i % NDB, kc = i / NDB;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
-      // spread 32 sums and 32 scale-FMAs over the MFMAs
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+        o[q][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], as_bf16x8(pw[q][kc]), o[q][db], 0, 0, 0);
+      // spread 32 sums and 32 scale-FMAs per query block over the fragments
       constexpr int NM = 4 * NDB;
       constexpr int PER = (32 + NM - 1) / NM;
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const int f = i * PER + u;
         if (f < 32) {
-          if (f & 1) ts1 += x[f >> 4][f & 15];
-          else ts0 += x[f >> 4][f & 15];
-          x[f >> 4][f & 15] = fmaf(sn[f >> 4][f & 15], cc, off);
+#pragma unroll
+          for (int q = 0; q < QB; ++q) {
+            ts[q][f & 1] += x[q][f >> 4][f & 15];
+            x[q][f >> 4][f & 15] = fmaf(sn[q][f >> 4][f & 15], cc, off[q]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lsum += ts0 + ts1;
-    if (wave_any(m_new > m_used)) {
-      // lazy rescale after the PV product of tile t (which used the old m)
-      const float alpha = fast_exp2(m_used - m_new);
-      lsum *= alpha;
+    bool any_grow = false;
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) o[i] *= alpha;
-      m_used = m_new;
+    for (int q = 0; q < QB; ++q) {
+      lsum[q] += ts[q][0] + ts[q][1];
+      any_grow |= m_new[q] > m_used[q];
+    }
+    if (wave_any(any_grow)) {
+      // lazy rescale after the PV product of tile t (which used the old m)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const float alpha = fast_exp2(m_used[q] - m_new[q]);
+        lsum[q] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) o[q][i] *= alpha;
+        m_used[q] = m_new[q];
+      }
     }
 
     // K_{t+2} and V_{t+1} (staged NS-2 iterations ago) have landed; newer DMAs may fly on
@@ -677,43 +744,49 @@ void attn_bf16_kernel(AttnArgs a) {
   wait_vm<0>();
 
   // epilogue
-  const float ltot = xor32_sum(lsum);
-  if (!qvalid) return;
-  const float inv = 1.0f / ltot;
-  const float lse = (m_used + __log2f(ltot)) * kLn2;
-  if (PART) {
-    float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int q = 0; q < QB; ++q) {
+    const float ltot = xor32_sum(lsum[q]);
+    if (!qvalid[q]) continue;
+    const float inv = 1.0f / ltot;
+    const float lse = (m_used[q] + __log2f(ltot)) * kLn2;
+    if (PART) {
+      float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]) * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 y;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = o[db][j * 4 + i] * inv;
-        *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = y;
-      }
-    if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = lse;
-  } else {
-    __bf16* op = static_cast<__bf16*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qrow * a.o_sn;
+        for (int j = 0; j < 4; ++j) {
+          f32x4 y;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+          for (int i = 0; i < 4; ++i) y[i] = o[q][db][j * 4 + i] * inv;
+          *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = y;
+        }
+      if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]] = lse;
+    } else {
+      __bf16* op = static_cast<__bf16*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qrow[q] * a.o_sn;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 y;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = (__bf16)(o[db][j * 4 + i] * inv);
-        *reinterpret_cast<bf16x4*>(op + db * 32 + j * 8 + hh * 4) = y;
-      }
-    if (hh == 0) a.lse[((int64_t)b * a.H + h) * N + qrow] = lse;
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = (__bf16)(o[q][db][j * 4 + i] * inv);
+          *reinterpret_cast<bf16x4*>(op + db * 32 + j * 8 + hh * 4) = y;
+        }
+      if (hh == 0) a.lse[((int64_t)b * a.H + h) * N + qrow[q]] = lse;
+    }
   }
 }
 
 #undef KBUF
 #undef VBUF
 
-constexpr int kWaves = 8;                 // waves per workgroup of the bf16 kernel
+// Workgroup shape of the bf16 kernel: kWaves waves, each owning kQB blocks of
+// 32 query rows (every LDS fragment then feeds kQB MFMAs).
+constexpr int kWaves = 8;
+constexpr int kQB = 1;
 
-int attn_bf16_block_q(int) { return kWaves * 32; }
+int attn_bf16_block_q(int) { return kWaves * kQB * 32; }
 
 int attn_bf16_grid(const AttnArgs& a) { return a.nqb * a.B * a.H; }
 
@@ -721,11 +794,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool partitioned, hipStrea
   dim3 grid(attn_bf16_grid(a), partitioned ? a.nparts : 1);
   dim3 block(kWaves * 64);
   if (D == 128) {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, false>), grid, block, 0, s, a);
+    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, kQB, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, kQB, false>), grid, block, 0, s, a);
   } else {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, false>), grid, block, 0, s, a);
+    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, kQB, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, kQB, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
