@@ -181,14 +181,19 @@ hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn
 
 // ------------------------------------------------------ key-tile norm bound
 // kmax[b*H + h][t] = max |k_n| over the 64 keys of tile t (rows past N repeat
-// row N-1, as the attention kernel's staging does). One wave per tile.
-__global__ __launch_bounds__(64) void knorm_kernel(const __bf16* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
-                                                   int H, int N, int D, int nkt, float* __restrict__ kmax) {
+// row N-1, as the attention kernel's staging does). 256 threads per tile: four
+// adjacent threads read one row's D/4 contiguous elements (coalesced), the
+// row's sum of squares is combined across them, then the max over the rows.
+__global__ __launch_bounds__(256) void knorm_kernel(const __bf16* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
+                                                    int H, int N, int D, int nkt, float* __restrict__ kmax) {
+  __shared__ float wmax[4];
   const int t = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int n = min(t * kBlockK + (int)threadIdx.x, N - 1);
-  const __bf16* kp = k + b * sb + h * sh + (int64_t)n * sn;
+  const int r = threadIdx.x >> 2, qd = threadIdx.x & 3;
+  const int n = min(t * kBlockK + r, N - 1);
+  const int dq = D / 4;
+  const __bf16* kp = k + b * sb + h * sh + (int64_t)n * sn + qd * dq;
   float ss = 0.0f;
-  for (int i = 0; i < D; i += 8) {
+  for (int i = 0; i < dq; i += 8) {
     const bf16x8 v = *reinterpret_cast<const bf16x8*>(kp + i);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -196,15 +201,20 @@ __global__ __launch_bounds__(64) void knorm_kernel(const __bf16* __restrict__ k,
       ss = fmaf(f, f, ss);
     }
   }
-  float r = sqrtf(ss);
-  for (int off = 32; off >= 1; off >>= 1) r = fmaxf(r, __shfl_xor(r, off));
-  if (threadIdx.x == 0) kmax[(int64_t)bh * nkt + t] = r;
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  float m = sqrtf(ss);
+  for (int off = 32; off >= 4; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    kmax[(int64_t)bh * nkt + t] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, float* kmax, int B, int H, int N,
                         int nkt, int D, hipStream_t s) {
   dim3 grid(nkt, B * H);
-  hipLaunchKernelGGL(knorm_kernel, grid, dim3(64), 0, s, k, sb, sh, sn, H, N, D, nkt, kmax);
+  hipLaunchKernelGGL(knorm_kernel, grid, dim3(256), 0, s, k, sb, sh, sn, H, N, D, nkt, kmax);
   return hipGetLastError();
 }
 
