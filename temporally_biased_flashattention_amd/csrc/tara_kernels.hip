@@ -234,66 +234,77 @@ constexpr int kStages = 3;
 // Key row held by S^T output row `r` of a 32-key block: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-__device__ __forceinline__ void dma16(const char* g, char* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// A byte range of global memory addressed by buffer instructions (raw
+// addressing, stride 0): loads past `bytes` return zeros instead of touching
+// other memory.
+struct BufRange {
+  const void* base;
+  uint32_t bytes;
+};
+
+// 16 bytes per lane from r.base + soff + voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(BufRange r, uint32_t voff, uint32_t soff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(r.base), 0, (int)r.bytes, 0x00020000),
+      (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-// Tile staging by LDS DMA (global_load_lds_dwordx4): one wave instruction
+// Tile staging by LDS DMA (buffer_load_dwordx4 ... lds): one wave instruction
 // writes 64 lanes x 16 bytes contiguously at a uniform LDS address. Every call
-// stages one padded K tile (64 rows of KROW elements) and one padded V^T tile
-// (D rows of VROW) as whole 1-KB blocks: combined block ci < KBLK is K, the
-// rest V^T, and wave w takes blocks w, w + NW, .... Every wave issues exactly
-// PER_WAVE DMAs per call (a wave with fewer blocks repeats its first block,
-// which rewrites the same bytes), so the issue is branch-free and the count of
-// pending DMAs is the same in every wave. A lane whose 16 bytes fall on a
-// row's pad chunk re-reads chunk 0 of its row (never read back).
+// stages one padded K tile (64 rows of KROWB bytes) and one padded V^T tile
+// (D rows of VROWB bytes) as whole 1-KB blocks: combined block ci < KBLK is K,
+// the rest V^T, and wave w takes blocks w, w + NW, ... (PER_MAX DMAs for waves
+// w < TOT % NW, PER_MIN for the others). A lane whose 16 bytes fall on a row's
+// pad chunk re-reads chunk 0 of its row (never read back). Buffer loads rather
+// than global_load_lds: the latter is FLAT-encoded, and while one is in flight
+// the compiler cannot count LDS reads, so every fragment wait drains them all.
 template <int KROWB, int KDATA, int KBLK, int VROWB, int VDATA, int VBLK, int NW>
 struct KvDma {
   static constexpr int TOT = KBLK + VBLK;
-  static constexpr int PER_WAVE = (TOT + NW - 1) / NW;
-  uint32_t goff[PER_WAVE];   // byte offset of this lane's 16 bytes in its global tile
-  int krow[PER_WAVE];        // K tile row of those bytes (for the tail clamp); -1 for V^T
-  __device__ void init(int wave, int lane, int64_t k_row_bytes, int64_t v_row_bytes) {
+  static constexpr int PER_MIN = TOT / NW;
+  static constexpr int PER_MAX = (TOT + NW - 1) / NW;
+  static constexpr int NEXTRA = TOT % NW;   // waves issuing PER_MAX
+  uint32_t voff[PER_MAX];   // byte offset of this lane's 16 bytes in its tile
+  int krow[PER_MAX];        // K tile row of those bytes (tail clamp)
+  __device__ void init(int wave, int lane, uint32_t k_row_bytes, uint32_t v_row_bytes) {
 #pragma unroll
-    for (int p = 0; p < PER_WAVE; ++p) {
-      const int ci = block(wave, p);
+    for (int p = 0; p < PER_MAX; ++p) {
+      const int ci = min(wave + p * NW, TOT - 1);
       if (ci < KBLK) {
         const int o = ci * 1024 + lane * 16, r = o / KROWB, c = (o % KROWB) / 16;
         krow[p] = r;
-        goff[p] = (uint32_t)(r * k_row_bytes + (c < KDATA ? c * 16 : 0));
+        voff[p] = r * k_row_bytes + (c < KDATA ? c * 16 : 0);
       } else {
         const int o = (ci - KBLK) * 1024 + lane * 16, d = o / VROWB, c = (o % VROWB) / 16;
-        krow[p] = -1;
-        goff[p] = (uint32_t)(d * v_row_bytes + (c < VDATA ? c * 16 : 0));
+        krow[p] = 0;
+        voff[p] = d * v_row_bytes + (c < VDATA ? c * 16 : 0);
       }
     }
   }
-  // combined block index of this wave's p-th DMA (uniform)
-  __device__ static int block(int wave, int p) {
-    const int ci = wave + p * NW;
-    return ci < TOT ? ci : wave;
+  // DMAs this wave issues per call (uniform)
+  __device__ static int count(int wave) { return wave < NEXTRA ? PER_MAX : PER_MIN; }
+  // K rows past the sequence (tail tile, rows_left < 64) re-read its last
+  // row; those keys are masked later. wave must be in [0, NW).
+  __device__ void issue(BufRange rk, uint32_t ksoff, int rows_left, uint32_t k_row_bytes, char* lds_k, BufRange rv,
+                        uint32_t vsoff, char* lds_v, int wave) const {
+    if (rows_left >= kBlockK) issue_blocks<false>(rk, ksoff, rows_left, k_row_bytes, lds_k, rv, vsoff, lds_v, wave);
+    else issue_blocks<true>(rk, ksoff, rows_left, k_row_bytes, lds_k, rv, vsoff, lds_v, wave);
   }
-  // K rows past the sequence (tail tile) re-read its last row; those keys are masked later.
-  __device__ void issue(const char* kg_tile, int rows_left, int64_t k_row_bytes, char* lds_k, const char* vg_tile,
-                        char* lds_v, int wave) const {
-    if (rows_left >= kBlockK) {
+  template <bool TAIL>
+  __device__ void issue_blocks(BufRange rk, uint32_t ksoff, int rows_left, uint32_t k_row_bytes, char* lds_k,
+                               BufRange rv, uint32_t vsoff, char* lds_v, int wave) const {
 #pragma unroll
-      for (int p = 0; p < PER_WAVE; ++p) {
-        const int ci = block(wave, p);
-        const bool isk = ci < KBLK;
-        const char* g = isk ? kg_tile : vg_tile;
-        char* l = isk ? lds_k + ci * 1024 : lds_v + (ci - KBLK) * 1024;
-        dma16(g + goff[p], l);
-      }
-    } else {
-#pragma unroll
-      for (int p = 0; p < PER_WAVE; ++p) {
-        const int ci = block(wave, p);
-        const bool isk = ci < KBLK;
-        const char* g = isk ? kg_tile - (int64_t)(krow[p] - min(krow[p], rows_left - 1)) * k_row_bytes : vg_tile;
-        char* l = isk ? lds_k + ci * 1024 : lds_v + (ci - KBLK) * 1024;
-        dma16(g + goff[p], l);
+    for (int p = 0; p < PER_MAX; ++p) {
+      if (p >= PER_MIN && wave >= NEXTRA) break;
+      const int ci = wave + p * NW;
+      // decided at compile time unless the blocks of step p straddle K and V^T
+      const bool isk = (p + 1) * NW <= KBLK ? true : p * NW >= KBLK ? false : ci < KBLK;
+      if (isk) {
+        uint32_t vo = voff[p];
+        if (TAIL) vo -= (uint32_t)(krow[p] - min(krow[p], rows_left - 1)) * k_row_bytes;
+        dma16(rk, vo, ksoff, lds_k + ci * 1024);
+      } else {
+        dma16(rv, voff[p], vsoff, lds_v + (ci - KBLK) * 1024);
       }
     }
   }
@@ -351,6 +362,14 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// Marks 16 values as used at this point (emits no instruction). The operands
+// are single floats: a 64-byte vector operand is not valid for the host pass,
+// which then silently drops the kernel's launch stub.
+__device__ __forceinline__ void keep16(const f32x16& v) {
+  asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+               "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+}
 
 typedef const __attribute__((address_space(4))) KeyTileSummary* KsumConstPtr;
 
@@ -441,7 +460,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int N = a.N;
 
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);   // uniform per wave
 
   // this lane's query rows: block q of the wave holds rows wave*32*QB + 32*q + lq
   int qrow[QB];
@@ -481,27 +500,33 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   const int kt0 = k0 / kBlockK, kt1 = (k1 + kBlockK - 1) / kBlockK;
 
-  // staging: 32-bit byte offsets from a per-tile scalar base
-  const char* kg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh);
-  const char* vg = reinterpret_cast<const char*>(a.vt + (int64_t)bh * D * a.npad);
-  const int64_t k_sn_bytes = a.k_sn * 2;
+  // staging: buffer resources over this head's K rows and V^T rows; per-lane
+  // 32-bit offsets within a tile, per-tile scalar offsets
+  const __bf16* kg = static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh;
+  const __bf16* vg = a.vt + (int64_t)bh * D * a.npad;
+  const uint32_t k_sn_bytes = (uint32_t)(a.k_sn * 2);
+  const BufRange rk{kg, (uint32_t)(N - 1) * k_sn_bytes + D * 2};
+  const BufRange rv{vg, (uint32_t)(D * a.npad * 2)};
   constexpr int KBLK = KTILE * 2 / 1024, VBLK = VTILE * 2 / 1024;
   static_assert(KBLK * 1024 == KTILE * 2 && VBLK * 1024 == VTILE * 2, "tiles are whole 1-KB blocks");
-  auto ktile_base = [&](int kt) { return kg + (int64_t)kt * kBlockK * k_sn_bytes; };
-  auto vtile_base = [&](int kt) { return vg + (int64_t)kt * kBlockK * 2; };
   using Dma = KvDma<KROW * 2, D / 8, KBLK, VROW * 2, kBlockK / 8, VBLK, NW>;
   Dma dma;
-  dma.init(wave, lane, k_sn_bytes, (int64_t)a.npad * 2);
+  dma.init(wave, lane, k_sn_bytes, (uint32_t)a.npad * 2);
+  const bool dma_extra = Dma::count(wave) == Dma::PER_MAX;
   // stage K tile kk into K slot sk and V^T tile kv into V slot sv (indices past
   // the range are clamped to its last tile: the slot is free either way)
   auto stage = [&](int kk, int sk, int kv, int sv) {
     kk = min(kk, kt1 - 1);
     kv = min(kv, kt1 - 1);
-    dma.issue(ktile_base(kk), N - kk * kBlockK, k_sn_bytes, reinterpret_cast<char*>(KBUF(sk)), vtile_base(kv),
-              reinterpret_cast<char*>(VBUF(sv)), wave);
+    dma.issue(rk, (uint32_t)kk * kBlockK * k_sn_bytes, N - kk * kBlockK, k_sn_bytes,
+              reinterpret_cast<char*>(KBUF(sk)), rv, (uint32_t)kv * kBlockK * 2, reinterpret_cast<char*>(VBUF(sv)),
+              wave);
   };
   // keep this iteration's DMAs (and those of the NS-3 before it) in flight
-  auto wait_staged = [&]() { wait_vm<(NS - 2) * Dma::PER_WAVE>(); };
+  auto wait_staged = [&]() {
+    if (dma_extra) wait_vm<(NS - 2) * Dma::PER_MAX>();
+    else wait_vm<(NS - 2) * Dma::PER_MIN>();
+  };
 
   const float* tkb = a.tk + (int64_t)b * a.npad;
   const float* kbb = a.kb + (int64_t)b * a.npad;
@@ -725,6 +750,12 @@ void attn_bf16_kernel(AttnArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // X_{t+1} belongs to phase B (its FMAs hide under the PV MFMAs): keep it
+    // from being sunk past the rescale branch
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) keep16(x[q][kb]);
     bool any_grow = false;
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
@@ -748,6 +779,10 @@ void attn_bf16_kernel(AttnArgs a) {
     sm_next = load_summary(ks_c, min(t + 2, kt1 - 1));
     kmax_next = kmax_c[min(t + 2, kt1 - 1)];
     __builtin_amdgcn_s_barrier();
+    // take the scalar loads here, where no LDS read is pending: a scalar load
+    // still in flight would turn every LDS fragment wait of the next
+    // iteration into a full drain (scalar loads complete out of order)
+    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.bias), "s"(kmax_next));
     s0 = s1;
   }
   // no DMA may still target this workgroup's LDS when it exits
