@@ -223,12 +223,16 @@ hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, flo
 // tile t every wave runs a two-phase software pipeline so that its MFMAs and
 // its softmax VALU work interleave in program order (MFMA and VALU of one wave
 // co-issue; in-order issue means the VALU work has to sit between the MFMAs):
-//   phase A: S_{t+1} = K_{t+1} Q^T (16 MFMAs)   with   P_t = exp2(X_t), row sums, bf16 pack
-//   phase B: O^T += V_t^T P_t^T (16 MFMAs)      with   max / bias class / X_{t+1} = S_{t+1} c + b - m
-// so K runs one tile ahead of V in LDS: iteration t reads K_{t+1} and V_t and
-// stages K_{t+2} and V_{t+1} (two LDS buffers each, one barrier per tile).
+//   phase A: S_{t+1} = K_{t+1} Q^T (16 MFMAs)   with   P_t = exp2(X_t) and its bf16 pack
+//   phase B: O^T += V_t^T P_t^T (16 MFMAs)      with   row sums of P_t, X_{t+1} = S_{t+1} c + b - m
+// K runs one tile ahead of V. One ring of LDS fragment registers is fetched
+// three fragments ahead through both phases and across iterations (the tail
+// of phase A fetches V_t, the tail of phase B fetches K_{t+2}), so no LDS
+// latency is exposed where a phase starts. Between the phases every wave
+// waits for its own DMAs of K_{t+2} and V_{t+1}, and the workgroup meets at
+// its one barrier per tile.
 
-// LDS ring depth of the bf16 kernel (K/V^T tile pairs in flight).
+// LDS ring depth of the bf16 kernel (K and V^T tiles).
 constexpr int kStages = 3;
 
 // Key row held by S^T output row `r` of a 32-key block: bits 2 and 3 swapped.
@@ -250,62 +254,42 @@ __device__ __forceinline__ void dma16(BufRange r, uint32_t voff, uint32_t soff, 
 }
 
 // Tile staging by LDS DMA (buffer_load_dwordx4 ... lds): one wave instruction
-// writes 64 lanes x 16 bytes contiguously at a uniform LDS address. Every call
-// stages one padded K tile (64 rows of KROWB bytes) and one padded V^T tile
-// (D rows of VROWB bytes) as whole 1-KB blocks: combined block ci < KBLK is K,
-// the rest V^T, and wave w takes blocks w, w + NW, ... (PER_MAX DMAs for waves
-// w < TOT % NW, PER_MIN for the others). A lane whose 16 bytes fall on a row's
-// pad chunk re-reads chunk 0 of its row (never read back). Buffer loads rather
-// than global_load_lds: the latter is FLAT-encoded, and while one is in flight
-// the compiler cannot count LDS reads, so every fragment wait drains them all.
-template <int KROWB, int KDATA, int KBLK, int VROWB, int VDATA, int VBLK, int NW>
-struct KvDma {
-  static constexpr int TOT = KBLK + VBLK;
-  static constexpr int PER_MIN = TOT / NW;
-  static constexpr int PER_MAX = (TOT + NW - 1) / NW;
-  static constexpr int NEXTRA = TOT % NW;   // waves issuing PER_MAX
+// writes 64 lanes x 16 bytes contiguously at a uniform LDS address. A padded
+// tile of BLK whole 1-KB blocks (rows of ROWB bytes holding DATA 16-byte data
+// chunks) is staged by all NW waves: wave w takes blocks w, w + NW, ...
+// (PER_MAX DMAs for waves w < BLK % NW, PER_MIN for the others). A lane whose
+// 16 bytes fall on a row's pad chunk re-reads chunk 0 of its row (never read
+// back). Buffer loads rather than global_load_lds: the latter is FLAT-encoded,
+// and while one is in flight the compiler cannot count LDS reads, so every
+// fragment wait would drain all of them.
+template <int ROWB, int DATA, int BLK, int NW>
+struct TileDma {
+  static constexpr int PER_MIN = BLK / NW;
+  static constexpr int PER_MAX = (BLK + NW - 1) / NW;
+  static constexpr int NEXTRA = BLK % NW;
+  static_assert(PER_MIN >= 1, "every wave stages at least one block");
   uint32_t voff[PER_MAX];   // byte offset of this lane's 16 bytes in its tile
-  int krow[PER_MAX];        // K tile row of those bytes (tail clamp)
-  __device__ void init(int wave, int lane, uint32_t k_row_bytes, uint32_t v_row_bytes) {
+  int row[PER_MAX];         // tile row of those bytes
+  __device__ void init(int wave, int lane, uint32_t row_bytes) {
 #pragma unroll
     for (int p = 0; p < PER_MAX; ++p) {
-      const int ci = min(wave + p * NW, TOT - 1);
-      if (ci < KBLK) {
-        const int o = ci * 1024 + lane * 16, r = o / KROWB, c = (o % KROWB) / 16;
-        krow[p] = r;
-        voff[p] = r * k_row_bytes + (c < KDATA ? c * 16 : 0);
-      } else {
-        const int o = (ci - KBLK) * 1024 + lane * 16, d = o / VROWB, c = (o % VROWB) / 16;
-        krow[p] = 0;
-        voff[p] = d * v_row_bytes + (c < VDATA ? c * 16 : 0);
-      }
+      const int ci = min(wave + p * NW, BLK - 1);
+      const int o = ci * 1024 + lane * 16, r = o / ROWB, c = (o % ROWB) / 16;
+      row[p] = r;
+      voff[p] = r * row_bytes + (c < DATA ? c * 16 : 0);
     }
   }
-  // DMAs this wave issues per call (uniform)
-  __device__ static int count(int wave) { return wave < NEXTRA ? PER_MAX : PER_MIN; }
-  // K rows past the sequence (tail tile, rows_left < 64) re-read its last
-  // row; those keys are masked later. wave must be in [0, NW).
-  __device__ void issue(BufRange rk, uint32_t ksoff, int rows_left, uint32_t k_row_bytes, char* lds_k, BufRange rv,
-                        uint32_t vsoff, char* lds_v, int wave) const {
-    if (rows_left >= kBlockK) issue_blocks<false>(rk, ksoff, rows_left, k_row_bytes, lds_k, rv, vsoff, lds_v, wave);
-    else issue_blocks<true>(rk, ksoff, rows_left, k_row_bytes, lds_k, rv, vsoff, lds_v, wave);
-  }
+  // Stage the tile at byte offset soff of r into lds (wave in [0, NW)). With
+  // TAIL, rows at or past rows_left re-read row rows_left - 1 (their keys are
+  // masked later).
   template <bool TAIL>
-  __device__ void issue_blocks(BufRange rk, uint32_t ksoff, int rows_left, uint32_t k_row_bytes, char* lds_k,
-                               BufRange rv, uint32_t vsoff, char* lds_v, int wave) const {
+  __device__ void issue(BufRange r, uint32_t soff, int rows_left, uint32_t row_bytes, char* lds, int wave) const {
 #pragma unroll
     for (int p = 0; p < PER_MAX; ++p) {
       if (p >= PER_MIN && wave >= NEXTRA) break;
-      const int ci = wave + p * NW;
-      // decided at compile time unless the blocks of step p straddle K and V^T
-      const bool isk = (p + 1) * NW <= KBLK ? true : p * NW >= KBLK ? false : ci < KBLK;
-      if (isk) {
-        uint32_t vo = voff[p];
-        if (TAIL) vo -= (uint32_t)(krow[p] - min(krow[p], rows_left - 1)) * k_row_bytes;
-        dma16(rk, vo, ksoff, lds_k + ci * 1024);
-      } else {
-        dma16(rv, voff[p], vsoff, lds_v + (ci - KBLK) * 1024);
-      }
+      uint32_t vo = voff[p];
+      if (TAIL) vo -= (uint32_t)(row[p] - min(row[p], rows_left - 1)) * row_bytes;
+      dma16(r, vo, soff, lds + (wave + p * NW) * 1024);
     }
   }
 };
@@ -437,18 +421,22 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
   }
 }
 
-template <int D, int NW, int QB, bool PART>
+template <int D, int NW, bool PART>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void attn_bf16_kernel(AttnArgs a) {
-  constexpr int BQ = NW * QB * 32;         // query rows per workgroup
+  constexpr int BQ = NW * 32;              // query rows per workgroup
   constexpr int KROW = D + 8;              // padded LDS pitch of a K row (elements)
   constexpr int VROW = kBlockK + 8;        // padded LDS pitch of a V^T row (elements)
   constexpr int KTILE = kBlockK * KROW;
   constexpr int VTILE = D * VROW;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
+  constexpr int NA = 2 * NKK;              // MFMAs (and LDS fragments) of phase A
+  constexpr int NB = 4 * NDB;              // MFMAs (and LDS fragments) of phase B
+  static_assert(NA % 4 == 0 && NB % 4 == 0, "ring positions carry over between the phases");
   // LDS ring of NS stages: K tiles in slots 0..NS-1, then V^T tiles in slots 0..NS-1
   constexpr int NS = kStages;
+  static_assert(NS == 3, "slot arithmetic and the DMA wait count assume three stages");
   __shared__ __attribute__((aligned(16))) __bf16 smem[NS * (KTILE + VTILE)];
 #define KBUF(i) (smem + (i) * KTILE)
 #define VBUF(i) (smem + NS * KTILE + (i) * VTILE)
@@ -462,376 +450,318 @@ void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);   // uniform per wave
 
-  // this lane's query rows: block q of the wave holds rows wave*32*QB + 32*q + lq
-  int qrow[QB];
-  bool qvalid[QB];
-  bf16x8 qf[QB][NKK];
-  float tq[QB], mq[QB];
-  bool qbiased[QB];
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    qrow[q] = qblk * BQ + (wave * QB + q) * 32 + lq;
-    qvalid[q] = qrow[q] < N;
-    const int qr = qvalid[q] ? qrow[q] : N - 1;
+  // this lane's query row: column lq of the wave's S^T blocks
+  const int qrow = qblk * BQ + wave * 32 + lq;
+  const bool qvalid = qrow < N;
+  const int qr = qvalid ? qrow : N - 1;
+  bf16x8 qf[NKK];
+  {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)qr * a.q_sn;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[q][kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
-    tq[q] = a.tq[(int64_t)b * N + qr];
-    mq[q] = a.mq[(int64_t)b * N + qr];
-    qbiased[q] = tq[q] == tq[q];
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
   }
+  const float tq = a.tq[(int64_t)b * N + qr];
+  const float mq = a.mq[(int64_t)b * N + qr];
+  const bool qbiased = tq == tq;
 
   const int k0 = a.kr[part], k1 = a.kr[part + 1];
   if (k1 <= k0) {
     // empty key range (partitioned mode only): contributes nothing to the merge
-    if (PART) {
+    if (PART && qvalid) {
+      float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
 #pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        if (!qvalid[q]) continue;
-        float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]) * D;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
-        if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]] = -INFINITY;
-      }
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
+      if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = -INFINITY;
     }
     return;
   }
   const int kt0 = k0 / kBlockK, kt1 = (k1 + kBlockK - 1) / kBlockK;
 
-  // staging: buffer resources over this head's K rows and V^T rows; per-lane
+  // staging: buffer ranges over this head's K rows and V^T rows; per-lane
   // 32-bit offsets within a tile, per-tile scalar offsets
   const __bf16* kg = static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh;
   const __bf16* vg = a.vt + (int64_t)bh * D * a.npad;
   const uint32_t k_sn_bytes = (uint32_t)(a.k_sn * 2);
   const BufRange rk{kg, (uint32_t)(N - 1) * k_sn_bytes + D * 2};
   const BufRange rv{vg, (uint32_t)(D * a.npad * 2)};
-  constexpr int KBLK = KTILE * 2 / 1024, VBLK = VTILE * 2 / 1024;
-  static_assert(KBLK * 1024 == KTILE * 2 && VBLK * 1024 == VTILE * 2, "tiles are whole 1-KB blocks");
-  using Dma = KvDma<KROW * 2, D / 8, KBLK, VROW * 2, kBlockK / 8, VBLK, NW>;
-  Dma dma;
-  dma.init(wave, lane, k_sn_bytes, (uint32_t)a.npad * 2);
-  const bool dma_extra = Dma::count(wave) == Dma::PER_MAX;
-  // stage K tile kk into K slot sk and V^T tile kv into V slot sv (indices past
-  // the range are clamped to its last tile: the slot is free either way)
-  auto stage = [&](int kk, int sk, int kv, int sv) {
+  static_assert(KTILE * 2 % 1024 == 0 && VTILE * 2 % 1024 == 0, "tiles are whole 1-KB blocks");
+  using KDma = TileDma<KROW * 2, D / 8, KTILE * 2 / 1024, NW>;
+  using VDma = TileDma<VROW * 2, kBlockK / 8, VTILE * 2 / 1024, NW>;
+  KDma kdma;
+  VDma vdma;
+  kdma.init(wave, lane, k_sn_bytes);
+  vdma.init(wave, lane, (uint32_t)a.npad * 2);
+  // K tile kk into K slot sk, V^T tile kv into V slot sv; indices past the
+  // range are clamped to its last tile (the slot is free either way)
+  auto stage_k = [&](int kk, int sk) {
     kk = min(kk, kt1 - 1);
-    kv = min(kv, kt1 - 1);
-    dma.issue(rk, (uint32_t)kk * kBlockK * k_sn_bytes, N - kk * kBlockK, k_sn_bytes,
-              reinterpret_cast<char*>(KBUF(sk)), rv, (uint32_t)kv * kBlockK * 2, reinterpret_cast<char*>(VBUF(sv)),
-              wave);
+    const int rows_left = N - kk * kBlockK;
+    const uint32_t soff = (uint32_t)kk * kBlockK * k_sn_bytes;
+    char* l = reinterpret_cast<char*>(KBUF(sk));
+    if (rows_left >= kBlockK) kdma.template issue<false>(rk, soff, rows_left, k_sn_bytes, l, wave);
+    else kdma.template issue<true>(rk, soff, rows_left, k_sn_bytes, l, wave);
   };
-  // keep this iteration's DMAs (and those of the NS-3 before it) in flight
+  auto stage_v = [&](int kv, int sv) {
+    kv = min(kv, kt1 - 1);
+    vdma.template issue<false>(rv, (uint32_t)kv * kBlockK * 2, kBlockK, 0, reinterpret_cast<char*>(VBUF(sv)), wave);
+  };
+  // this wave's DMAs of K_{t+2} and V_{t+1} have landed; those of K_{t+3},
+  // issued after them, may stay in flight
   auto wait_staged = [&]() {
-    if (dma_extra) wait_vm<(NS - 2) * Dma::PER_MAX>();
-    else wait_vm<(NS - 2) * Dma::PER_MIN>();
+    if (wave < KDma::NEXTRA) wait_vm<KDma::PER_MAX>();
+    else wait_vm<KDma::PER_MIN>();
   };
 
   const float* tkb = a.tk + (int64_t)b * a.npad;
   const float* kbb = a.kb + (int64_t)b * a.npad;
-  const KeyTileSummary* ks_b = a.ksum + (int64_t)b * a.nkt;
-  // the same summaries through the constant address space: uniform loads of
-  // them become scalar loads
-  const KsumConstPtr ks_c = (KsumConstPtr)ks_b;
-  const int krow_lane = perm32(lq);
-  KeyTileSummary sm_next;
-  // max over each key tile of |k| (this head), for the row-max bound
+  // tile summaries and key norms through the constant address space: uniform
+  // loads of them become scalar loads
+  const KsumConstPtr ks_c = (KsumConstPtr)(a.ksum + (int64_t)b * a.nkt);
   const __attribute__((address_space(4))) float* kmax_c =
       (const __attribute__((address_space(4))) float*)(a.kmax + (int64_t)bh * a.nkt);
-  float kmax_next;
+  const int krow_lane = perm32(lq);
   // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum
-  float qn_c[QB];
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
+  float qn_c;
+  {
     float ss = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = (float)qf[q][kk][e];
+        const float v = (float)qf[kk][e];
         ss = fmaf(v, v, ss);
       }
-    qn_c[q] = sqrtf(xor32_sum(ss)) * a.c * (1.0f + 0x1.0p-10f);
+    qn_c = sqrtf(xor32_sum(ss)) * a.c * (1.0f + 0x1.0p-10f);
   }
 
-  f32x16 o[QB][NDB];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int q = 0; q < QB; ++q)
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) o[q][i] = f32x16{};
-  float m_used[QB], lsum[QB];
-  f32x16 x[QB][2];   // X_t = S_t * c + bias - m_used (exp2 argument)
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    m_used[q] = -INFINITY;
-    lsum[q] = 0.0f;
-  }
+  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+  float m_used, lsum = 0.0f;
+  f32x16 x[2];   // X_t = S_t * c + bias - m_used (exp2 argument)
+  KeyTileSummary sm_next;
+  float kmax_next;
+  // LDS fragment ring: fragment j of the per-wave stream (K_{t+1} fragments of
+  // phase A, then V_t fragments of phase B, then K_{t+2} ...) sits in fr[j & 3]
+  bf16x8 fr[4];
+  const int koff_lane = krow_lane * KROW + hh * 8;   // phase A reads K rows kb*32 + perm32(lq)
+  const int voff_lane = lq * VROW + hh * 8;          // phase B reads V^T rows db*32 + lq
 
   {
-    // prologue: K and V^T of tiles t0 .. t0+NS-1 into slots 0 .. NS-1; S_t0; X_t0
-#pragma unroll
-    for (int i = 0; i < NS; ++i) stage(kt0 + i, i, kt0 + i, i);
+    // prologue: K_t0..K_t0+2 into K slots 0..2, V_t0 and V_t0+1 into V slots
+    // 0 and 1; S_t0 and X_t0; the first three K_{t0+1} fragments
+    stage_k(kt0, 0);
+    stage_k(kt0 + 1, 1);
+    stage_k(kt0 + 2, 2);
+    stage_v(kt0, 0);
+    stage_v(kt0 + 1, 1);
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int q = 0; q < QB; ++q) qk_tile<D, KROW>(x[q], KBUF(0), krow_lane, hh, qf[q]);
+    qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
     const int kbase = kt0 * kBlockK;
     const bool partial = kbase < k0 || kbase + kBlockK > k1;
     const KeyTileSummary sm0 = load_summary(ks_c, kt0);
-    float brow[QB];
-    bool lane_elem = false;
-#pragma unroll
-    for (int q = 0; q < QB; ++q) lane_elem |= tile_class_lane(sm0, partial, qbiased[q], tq[q], mq[q], a, &brow[q]);
+    float brow;
+    const bool lane_elem = tile_class_lane(sm0, partial, qbiased, tq, mq, a, &brow);
     float cc = a.c;
     if (wave_any(lane_elem)) {
-#pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        elem_bias(x[q], kbase, hh, tq[q], mq[q], partial, k0, k1, tkb, kbb, a);
-        brow[q] = 0.0f;
-      }
+      elem_bias(x, kbase, hh, tq, mq, partial, k0, k1, tkb, kbb, a);
+      brow = 0.0f;
       cc = 1.0f;
     }
+    float mx = x[0][0];
 #pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      float mx = x[q][0][0];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+    m_used = fmaf(xor32_max(mx), cc, brow);
+    const float off = brow - m_used;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[q][kb][r]);
-      m_used[q] = fmaf(xor32_max(mx), cc, brow[q]);
-      const float off = brow[q] - m_used[q];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[q][kb][r] = fmaf(x[q][kb][r], cc, off);
-    }
+      for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(x[kb][r], cc, off);
     sm_next = load_summary(ks_c, min(kt0 + 1, kt1 - 1));
     kmax_next = kmax_c[min(kt0 + 1, kt1 - 1)];
-    // every wave is done with K slot 0 before iteration 0 restages it
+    const __bf16* kr0 = KBUF(1) + koff_lane;
+    fr[0] = kfrag<KROW>(kr0, 0);
+    fr[1] = kfrag<KROW>(kr0, 1);
+    fr[2] = kfrag<KROW>(kr0, 2);
+    // every wave is done with K slot 0 before iteration t0 restages it
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.bias), "s"(kmax_next));
   }
 
-  // ring slots: iteration t reads K_{t+1} (slot s1) and V_t (slot s0), and
-  // restages K_{t+NS} into slot s0 (K_t's, read last iteration) and
-  // V_{t+NS-1} into slot sprev (V_{t-1}'s, read last iteration)
+  // ring slots at iteration t: K_t, V_t in s0; K_{t+1}, V_{t+1} in s1; K_{t+2}
+  // and V_{t-1} in s2. K_{t+3} is staged into s0 at the start (K_t was last
+  // read before the previous barrier), V_{t+2} into s2 after this iteration's
+  // barrier (V_{t-1} was last read before it).
   int s0 = 0;
   for (int t = kt0; t < kt1; ++t) {
     const bool has1 = t + 1 < kt1;
     const int s1 = s0 + 1 == NS ? 0 : s0 + 1;
-    const int sprev = s0 == 0 ? NS - 1 : s0 - 1;
-    stage(t + NS, s0, t + NS - 1, sprev);
-    const __bf16* kn = KBUF(s1);
-    const __bf16* vc = VBUF(s0);
+    const int s2 = s1 + 1 == NS ? 0 : s1 + 1;
+    stage_k(t + NS, s0);
     const int kbase1 = (t + 1) * kBlockK;
     const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
     const KeyTileSummary sm1 = sm_next;
     const float kmax1 = kmax_next;
+    const __bf16* kr0 = KBUF(s1) + koff_lane;   // K_{t+1}
+    const __bf16* vr0 = VBUF(s0) + voff_lane;   // V_t
+    const __bf16* kn0 = KBUF(s2) + koff_lane;   // K_{t+2}
 
-    // phase A: S_{t+1} = K_{t+1} Q^T (each K fragment feeds the QB query
-    // blocks; the two 32-key blocks alternate) | P_t = exp2(X_t) in place and
-    // its bf16 pack. K fragments are read from LDS three fragments ahead.
-    f32x16 sn[QB][2];
-#pragma unroll
-    for (int q = 0; q < QB; ++q) sn[q][0] = sn[q][1] = f32x16{};
-    const __bf16* kr0 = kn + krow_lane * KROW + hh * 8;
-    bf16x8 kf[4];
-    kf[0] = kfrag<KROW>(kr0, 0);
-    kf[1] = kfrag<KROW>(kr0, 1);
-    kf[2] = kfrag<KROW>(kr0, 2);
-    u32x4 pw[QB][4];   // P_t as packed bf16 pairs: pw[q][kb*2 + c2] is the B operand of PV block (kb, c2)
-    auto exp_pair = [&](int q, int i) {
-      // elements 2i, 2i+1 of the lane's 32 scores of tile t (query block q)
+    // phase A: S_{t+1} = K_{t+1} Q^T (the two 32-key blocks alternate) |
+    // P_t = exp2(X_t) in place and its bf16 pack. The ring runs three
+    // fragments ahead; its last three fetches are phase B's first V_t fragments.
+    f32x16 sn[2];
+    sn[0] = sn[1] = f32x16{};
+    u32x4 pw[4];   // P_t as packed bf16 pairs: pw[kb*2 + c2] is the B operand of PV chunk (kb, c2)
+    auto exp_pair = [&](int i) {
+      // elements 2i, 2i+1 of the lane's 32 scores of tile t
       const int kb = i >> 3, r = (2 * i) & 15;
-      const float p0 = fast_exp2(x[q][kb][r]), p1 = fast_exp2(x[q][kb][r + 1]);
-      x[q][kb][r] = p0;
-      x[q][kb][r + 1] = p1;
-      pw[q][i >> 2][i & 3] = pack_bf16x2(p0, p1);
+      const float p0 = fast_exp2(x[kb][r]), p1 = fast_exp2(x[kb][r + 1]);
+      x[kb][r] = p0;
+      x[kb][r + 1] = p1;
+      pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
     };
 #pragma unroll
-    for (int i = 0; i < 2 * NKK; ++i) {
-      if (i + 3 < 2 * NKK) kf[(i + 3) & 3] = kfrag<KROW>(kr0, i + 3);
-#pragma unroll
-      for (int q = 0; q < QB; ++q)
-        sn[q][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[q][i >> 1], sn[q][i & 1], 0, 0, 0);
-      if (i < 16) {
-#pragma unroll
-        for (int q = 0; q < QB; ++q) exp_pair(q, i);
-      }
+    for (int i = 0; i < NA; ++i) {
+      const int j = i + 3;
+      if (j < NA) fr[j & 3] = kfrag<KROW>(kr0, j);
+      else fr[j & 3] = vfrag<VROW, NDB>(vr0, j - NA);
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
+      if (i < 16) exp_pair(i);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 2 * NKK; i < 16; ++i)
-#pragma unroll
-      for (int q = 0; q < QB; ++q) exp_pair(q, i);
+    for (int i = NA; i < 16; ++i) exp_pair(i);
     // keep P_t in this block (the PV product that reads it follows the
     // bias-class branch)
-#pragma unroll
-    for (int q = 0; q < QB; ++q) asm volatile("" ::"v"(pw[q][0]), "v"(pw[q][1]), "v"(pw[q][2]), "v"(pw[q][3]));
+    asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]));
 
     // bias class of tile t+1 (rare per-element path before phase B)
-    float brow[QB];
+    float brow = 0.0f;
     float cc = a.c;
     bool need_max = false;
-#pragma unroll
-    for (int q = 0; q < QB; ++q) brow[q] = 0.0f;
     if (has1) {
-      bool lane_elem = false;
-#pragma unroll
-      for (int q = 0; q < QB; ++q)
-        lane_elem |= tile_class_lane(sm1, partial1, qbiased[q], tq[q], mq[q], a, &brow[q]);
+      const bool lane_elem = tile_class_lane(sm1, partial1, qbiased, tq, mq, a, &brow);
       if (wave_any(lane_elem)) {
-#pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          elem_bias(sn[q], kbase1, hh, tq[q], mq[q], partial1, k0, k1, tkb, kbb, a);
-          brow[q] = 0.0f;
-        }
+        elem_bias(sn, kbase1, hh, tq, mq, partial1, k0, k1, tkb, kbb, a);
+        brow = 0.0f;
         cc = 1.0f;
         need_max = true;
       } else {
         // every logit of the tile is <= |q| max|k| c + brow (Cauchy-Schwarz);
         // the exact row max is needed only when that bound could pass m + tau
-        bool lane_need = false;
-#pragma unroll
-        for (int q = 0; q < QB; ++q) lane_need |= fmaf(qn_c[q], kmax1, brow[q]) > m_used[q] + kRescaleTau;
-        need_max = wave_any(lane_need);
+        need_max = wave_any(fmaf(qn_c, kmax1, brow) > m_used + kRescaleTau);
       }
     }
-    float m_new[QB], off[QB];
-#pragma unroll
-    for (int q = 0; q < QB; ++q) m_new[q] = m_used[q];
+    float m_new = m_used;
     if (need_max) {
+      float mxa = -INFINITY, mxb = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        float mxa = -INFINITY, mxb = -INFINITY;
-#pragma unroll
-        for (int f = 0; f < 32; f += 4) {
-          mxa = max3f(mxa, sn[q][f >> 4][f & 15], sn[q][f >> 4][(f & 15) + 1]);
-          mxb = max3f(mxb, sn[q][f >> 4][(f & 15) + 2], sn[q][f >> 4][(f & 15) + 3]);
-        }
-        const float mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow[q]);
-        if (mt > m_used[q] + kRescaleTau) m_new[q] = mt;
+      for (int f = 0; f < 32; f += 4) {
+        mxa = max3f(mxa, sn[f >> 4][f & 15], sn[f >> 4][(f & 15) + 1]);
+        mxb = max3f(mxb, sn[f >> 4][(f & 15) + 2], sn[f >> 4][(f & 15) + 3]);
       }
+      const float mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow);
+      if (mt > m_used + kRescaleTau) m_new = mt;
     }
-#pragma unroll
-    for (int q = 0; q < QB; ++q) off[q] = brow[q] - m_new[q];
+    const float off = brow - m_new;
 
-    // phase B: O^T += V_t^T P_t^T (each V^T fragment feeds the QB query
-    // blocks) | row sum of P_t, X_{t+1} = S_{t+1} c + brow - m_new. V^T
-    // fragments are read three fragments ahead.
-    const __bf16* vr0 = vc + lq * VROW + hh * 8;
-    bf16x8 vf[4];
-    vf[0] = vfrag<VROW, NDB>(vr0, 0);
-    vf[1] = vfrag<VROW, NDB>(vr0, 1);
-    vf[2] = vfrag<VROW, NDB>(vr0, 2);
-    float ts[QB][2];
+    // K_{t+2} and V_{t+1} have landed for every wave past this barrier; the
+    // scalar loads are taken right after it, where no LDS read is pending (a
+    // scalar load in flight would turn the fragment waits of phase B into
+    // full drains: scalar loads complete out of order)
+    wait_staged();
+    sm_next = load_summary(ks_c, min(t + 2, kt1 - 1));
+    kmax_next = kmax_c[min(t + 2, kt1 - 1)];
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.bias), "s"(kmax_next));
+    stage_v(t + NS - 1, s2);
+
+    // phase B: O^T += V_t^T P_t^T | row sum of P_t, X_{t+1} = S_{t+1} c +
+    // brow - m_new. The ring's last three fetches are the next phase A's
+    // first K_{t+2} fragments.
+    float ts0 = 0.0f, ts1 = 0.0f;
 #pragma unroll
-    for (int q = 0; q < QB; ++q) ts[q][0] = ts[q][1] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4 * NDB; ++i) {
-      if (i + 3 < 4 * NDB) vf[(i + 3) & 3] = vfrag<VROW, NDB>(vr0, i + 3);
+    for (int i = 0; i < NB; ++i) {
+      const int j = i + 3;
+      if (j < NB) fr[j & 3] = vfrag<VROW, NDB>(vr0, j);
+      else fr[j & 3] = kfrag<KROW>(kn0, j - NB);
       const int db = i % NDB, kc = i / NDB;
-#pragma unroll
-      for (int q = 0; q < QB; ++q)
-        o[q][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], as_bf16x8(pw[q][kc]), o[q][db], 0, 0, 0);
-      // spread 32 sums and 32 scale-FMAs per query block over the fragments
-      constexpr int NM = 4 * NDB;
-      constexpr int PER = (32 + NM - 1) / NM;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
+      // spread 32 sums and 32 scale-FMAs over the fragments
+      constexpr int PER = (32 + NB - 1) / NB;
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const int f = i * PER + u;
         if (f < 32) {
-#pragma unroll
-          for (int q = 0; q < QB; ++q) {
-            ts[q][f & 1] += x[q][f >> 4][f & 15];
-            x[q][f >> 4][f & 15] = fmaf(sn[q][f >> 4][f & 15], cc, off[q]);
-          }
+          if (f & 1) ts1 += x[f >> 4][f & 15];
+          else ts0 += x[f >> 4][f & 15];
+          x[f >> 4][f & 15] = fmaf(sn[f >> 4][f & 15], cc, off);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // X_{t+1} belongs to phase B (its FMAs hide under the PV MFMAs): keep it
     // from being sunk past the rescale branch
-#pragma unroll
-    for (int q = 0; q < QB; ++q)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) keep16(x[q][kb]);
-    bool any_grow = false;
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      lsum[q] += ts[q][0] + ts[q][1];
-      any_grow |= m_new[q] > m_used[q];
-    }
-    if (wave_any(any_grow)) {
+    keep16(x[0]);
+    keep16(x[1]);
+    lsum += ts0 + ts1;
+    if (wave_any(m_new > m_used)) {
       // lazy rescale after the PV product of tile t (which used the old m)
+      const float alpha = fast_exp2(m_used - m_new);
+      lsum *= alpha;
 #pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        const float alpha = fast_exp2(m_used[q] - m_new[q]);
-        lsum[q] *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) o[q][i] *= alpha;
-        m_used[q] = m_new[q];
-      }
+      for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+      m_used = m_new;
     }
-
-    // K_{t+2} and V_{t+1} (staged NS-2 iterations ago) have landed; newer DMAs may fly on
-    wait_staged();
-    sm_next = load_summary(ks_c, min(t + 2, kt1 - 1));
-    kmax_next = kmax_c[min(t + 2, kt1 - 1)];
-    __builtin_amdgcn_s_barrier();
-    // take the scalar loads here, where no LDS read is pending: a scalar load
-    // still in flight would turn every LDS fragment wait of the next
-    // iteration into a full drain (scalar loads complete out of order)
-    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.bias), "s"(kmax_next));
     s0 = s1;
   }
   // no DMA may still target this workgroup's LDS when it exits
   wait_vm<0>();
 
   // epilogue
+  const float ltot = xor32_sum(lsum);
+  if (!qvalid) return;
+  const float inv = 1.0f / ltot;
+  const float lse = (m_used + __log2f(ltot)) * kLn2;
+  if (PART) {
+    float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const float ltot = xor32_sum(lsum[q]);
-    if (!qvalid[q]) continue;
-    const float inv = 1.0f / ltot;
-    const float lse = (m_used[q] + __log2f(ltot)) * kLn2;
-    if (PART) {
-      float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]) * D;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int j = 0; j < 4; ++j) {
+        f32x4 y;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 y;
+        for (int i = 0; i < 4; ++i) y[i] = o[db][j * 4 + i] * inv;
+        *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = y;
+      }
+    if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = lse;
+  } else {
+    __bf16* op = static_cast<__bf16*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qrow * a.o_sn;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = o[q][db][j * 4 + i] * inv;
-          *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = y;
-        }
-      if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow[q]] = lse;
-    } else {
-      __bf16* op = static_cast<__bf16*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qrow[q] * a.o_sn;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 y;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 y;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = (__bf16)(o[q][db][j * 4 + i] * inv);
-          *reinterpret_cast<bf16x4*>(op + db * 32 + j * 8 + hh * 4) = y;
-        }
-      if (hh == 0) a.lse[((int64_t)b * a.H + h) * N + qrow[q]] = lse;
-    }
+        for (int i = 0; i < 4; ++i) y[i] = (__bf16)(o[db][j * 4 + i] * inv);
+        *reinterpret_cast<bf16x4*>(op + db * 32 + j * 8 + hh * 4) = y;
+      }
+    if (hh == 0) a.lse[((int64_t)b * a.H + h) * N + qrow] = lse;
   }
 }
 
 #undef KBUF
 #undef VBUF
 
-// Workgroup shape of the bf16 kernel: kWaves waves, each owning kQB blocks of
-// 32 query rows (every LDS fragment then feeds kQB MFMAs).
+// Workgroup shape of the bf16 kernel: kWaves waves of 32 query rows.
 constexpr int kWaves = 8;
-constexpr int kQB = 1;
 
-int attn_bf16_block_q(int) { return kWaves * kQB * 32; }
+int attn_bf16_block_q(int) { return kWaves * 32; }
 
 int attn_bf16_grid(const AttnArgs& a) { return a.nqb * a.B * a.H; }
 
@@ -839,11 +769,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool partitioned, hipStrea
   dim3 grid(attn_bf16_grid(a), partitioned ? a.nparts : 1);
   dim3 block(kWaves * 64);
   if (D == 128) {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, kQB, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, kQB, false>), grid, block, 0, s, a);
+    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, false>), grid, block, 0, s, a);
   } else {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, kQB, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, kQB, false>), grid, block, 0, s, a);
+    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
