@@ -19,7 +19,9 @@ What it follows (page titles and sections of the TARA sources):
   * "BFS H3 Reference Attention Binding (Experimental)", section "The exact
     rule": a target query with mask weight m attending a key of Picture i gets
     m * log(gain_i) added to its logit before the shared softmax over all keys;
-    section "Inputs you'll set": no mask means m = 1 on the whole output video.
+    section "Inputs you'll set": no mask means m = 1 on the whole output video;
+    section "Common issues": chained binding nodes add their log gains, so J
+    bindings give sum_j m_j * log(gain_j,i).
   * LSE is the natural-log log-sum-exp of each query row's final logits, the
     quantity FlashAttention-with-LSE returns and the "Three backends" section
     merges across partitions.
@@ -71,7 +73,9 @@ def bias_block(seg_q, time_q, mask_q, seg_k, time_k, pic_k, params) -> np.ndarra
 
     Target-query x guide-key entries get -penalty(|t_q - t_k|). When binding is
     enabled, target-query x picture-key entries get m_q * ln(gain[picture]),
-    m_q = 1 when no mask is given. Every other entry is 0.
+    m_q = 1 when no mask is given; with chained bindings the terms of every
+    binding j are added, sum_j m_j,q * ln(gain_j[picture]) (mask_q is then
+    [J, R], one plane per binding). Every other entry is 0.
     """
     seg_q = np.asarray(seg_q)
     seg_k = np.asarray(seg_k)
@@ -88,13 +92,17 @@ def bias_block(seg_q, time_q, mask_q, seg_k, time_k, pic_k, params) -> np.ndarra
     if params.binding:
         pk = np.nonzero(seg_k == PICTURE)[0]
         if pk.size:
-            gains = np.asarray(params.gains, dtype=np.float64)
-            if np.any(gains <= 0.0):
-                raise ValueError("gains must be > 0 (log of the gain)")
-            lg = np.log(gains[np.asarray(pic_k)[pk].astype(np.int64)])
-            m = (np.ones(rows.size) if mask_q is None
-                 else np.asarray(mask_q, np.float64)[rows])
-            bm[np.ix_(rows, pk)] = m[:, None] * lg[None, :]
+            ids = np.asarray(pic_k)[pk].astype(np.int64)
+            nb = getattr(params, "num_bindings", 1)
+            planes = None if mask_q is None else np.asarray(mask_q, np.float64).reshape(nb, -1)
+            gain_sets = params.all_gains() if hasattr(params, "all_gains") else (tuple(params.gains),)
+            for j, gains in enumerate(gain_sets):
+                gains = np.asarray(gains, dtype=np.float64)
+                if np.any(gains <= 0.0):
+                    raise ValueError("gains must be > 0 (log of the gain)")
+                lg = np.log(gains[ids])
+                m = np.ones(rows.size) if planes is None else planes[j][rows]
+                bm[np.ix_(rows, pk)] += m[:, None] * lg[None, :]
     return bm
 
 
@@ -129,7 +137,7 @@ def attention_head(q, k, v, seg, time, picture, mask, params,
     for s in range(0, rows.size, chunk):
         r = rows[s:s + chunk]
         z = (q[r] @ kk.T) * sc
-        z += bias_block(seg[r], np.asarray(time)[r], None if mask is None else np.asarray(mask)[r],
+        z += bias_block(seg[r], np.asarray(time)[r], None if mask is None else np.asarray(mask)[..., r],
                         seg[k0:k1], np.asarray(time)[k0:k1], np.asarray(picture)[k0:k1], params)
         zmax = z.max(axis=1, keepdims=True)
         l = np.log(np.exp(z - zmax).sum(axis=1)) + zmax[:, 0]
@@ -141,7 +149,7 @@ def attention_head(q, k, v, seg, time, picture, mask, params,
 
 def attention(q, k, v, seg, time, picture, mask, params, rows=None, key_range=None,
               scale=None) -> Tuple[np.ndarray, np.ndarray]:
-    """Batched form: q, k, v [B, H, N, D]; metadata [B, N] (mask [B, N] or None).
+    """Batched form: q, k, v [B, H, N, D]; metadata [B, N] (mask [B, N], [J, B, N] or None).
 
     Returns O [B, H, R, D] and LSE [B, H, R] in fp64.
     """
@@ -154,8 +162,8 @@ def attention(q, k, v, seg, time, picture, mask, params, rows=None, key_range=No
         for hi in range(h):
             o[bi, hi], lse[bi, hi] = attention_head(
                 q[bi, hi], k[bi, hi], v[bi, hi], seg[bi], time[bi], picture[bi],
-                None if mask is None else mask[bi], params, rows=rows, key_range=key_range,
-                scale=scale)
+                None if mask is None else np.asarray(mask)[..., bi, :], params, rows=rows,
+                key_range=key_range, scale=scale)
     return o, lse
 
 
@@ -192,8 +200,14 @@ def attention_bruteforce(q, k, v, seg, time, picture, mask, params, scale=None):
                 x = max(dt - params.window, 0.0) / params.falloff
                 z -= min(params.strength * x * x, params.cap)
             if params.binding and int(seg[i]) == TARGET and int(seg[j]) == PICTURE:
-                m = 1.0 if mask is None else float(mask[i])
-                z += m * math.log(params.gains[int(picture[j])])
+                gain_sets = params.all_gains() if hasattr(params, "all_gains") else (tuple(params.gains),)
+                for b, gains in enumerate(gain_sets):
+                    if mask is None:
+                        m = 1.0
+                    else:
+                        mk = np.asarray(mask)
+                        m = float(mk[i]) if mk.ndim == 1 else float(mk[b][i])
+                    z += m * math.log(gains[int(picture[j])])
             zs.append(z)
         zm = max(zs)
         lse = zm + math.log(math.fsum(math.exp(z - zm) for z in zs))

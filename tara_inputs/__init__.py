@@ -44,12 +44,24 @@ class Params:
     cap: float = 6.0
     binding: bool = False
     gains: Sequence[float] = ()          # gain per 0-based picture id
+    # further bindings applied together with the first (chained binding
+    # nodes): one gain tuple per extra binding, same picture ids
+    chained: Sequence[Sequence[float]] = ()
+
+    @property
+    def num_bindings(self) -> int:
+        return 1 + len(self.chained)
+
+    def all_gains(self):
+        """Gain tuples of every binding, the first binding first."""
+        return (tuple(self.gains),) + tuple(tuple(g) for g in self.chained)
 
     def f32(self) -> "Params":
         """The same controls rounded to fp32, as a GPU receives them."""
         r = lambda x: float(np.float32(x))
         return Params(r(self.window), r(self.falloff), r(self.strength), r(self.cap),
-                      bool(self.binding), tuple(r(g) for g in self.gains))
+                      bool(self.binding), tuple(r(g) for g in self.gains),
+                      tuple(tuple(r(g) for g in c) for c in self.chained))
 
 
 @dataclasses.dataclass
@@ -59,7 +71,9 @@ class Layout:
     time: np.ndarray         # float32 [N], NaN where the token has no time
     picture: np.ndarray      # int16 [N], picture id for pictures, -1 elsewhere
     frame: np.ndarray        # int32 [N], latent frame for video tokens, -1 elsewhere
-    mask: Optional[np.ndarray] = None   # float32 [N] mask weight m (target tokens), else None
+    # float32 mask weight m of target tokens: [N] for one binding, [J, N] for J
+    # chained bindings (one plane per binding); None means m = 1 everywhere
+    mask: Optional[np.ndarray] = None
 
     @property
     def n(self) -> int:
@@ -68,7 +82,7 @@ class Layout:
     def permuted(self, perm: np.ndarray) -> "Layout":
         return Layout(self.seg[perm].copy(), self.time[perm].copy(), self.picture[perm].copy(),
                       self.frame[perm].copy(),
-                      None if self.mask is None else self.mask[perm].copy())
+                      None if self.mask is None else self.mask[..., perm].copy())
 
 
 def frame_time(f: np.ndarray) -> np.ndarray:

@@ -359,6 +359,94 @@ def test_p10_monotone_guide_mass():
             assert np.all(sign * (b - a) >= -1e-15), name
 
 
+# ------------------------------------------------ P11: chained bindings
+# "BFS H3 Reference Attention Binding (Experimental)", section "Common issues":
+# chained binding nodes add their log gains, so picture i's unnormalised weight
+# for a target row is multiplied by prod_j gain_j,i ** m_j.
+def _two_plane_mask(lay, rng):
+    tgt = lay.seg == ti.SEG_TARGET
+    planes = np.zeros((2, lay.n), dtype=np.float32)
+    planes[0, tgt] = rng.uniform(0.0, 1.0, int(tgt.sum()))
+    planes[1, tgt] = rng.uniform(0.0, 1.0, int(tgt.sum()))
+    return planes
+
+
+def test_p11_equal_masks_multiply_gains():
+    rng = np.random.default_rng(11)
+    lay = ti.make_layout(4, (3, 3), (3, 3), 3, 6, 5, mask=True)
+    q, k, v = (rng.standard_normal((lay.n, 12)) for _ in range(3))
+    g1, g2 = (1.6, 0.7, 1.1), (0.5, 1.9, 1.3)
+    both = np.stack([lay.mask, lay.mask])
+    o2, l2 = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, both,
+                                   ti.Params(binding=True, gains=g1, chained=(g2,)))
+    o1, l1 = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, lay.mask,
+                                   ti.Params(binding=True, gains=tuple(a * b for a, b in zip(g1, g2))))
+    assert np.max(np.abs(o2 - o1)) < 1e-12 and np.max(np.abs(l2 - l1)) < 1e-12
+
+
+def test_p11_neutral_chained_binding_bit_identical():
+    rng = np.random.default_rng(12)
+    lay = ti.make_layout(4, (3, 3), (3, 3), 2, 6, 5, mask=True)
+    q, k, v = (rng.standard_normal((lay.n, 8)) for _ in range(3))
+    g = (1.3, 0.8)
+    o1, l1 = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, lay.mask,
+                                   ti.Params(binding=True, gains=g))
+    zero_plane = np.stack([lay.mask, np.zeros_like(lay.mask)])
+    for mask, chained in ((np.stack([lay.mask, lay.mask]), ((1.0, 1.0),)),      # gain 1 is neutral
+                          (zero_plane, ((2.5, 0.3),))):                          # m = 0 is neutral
+        o2, l2 = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, mask,
+                                       ti.Params(binding=True, gains=g, chained=chained))
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_p11_q0_closed_form_two_bindings():
+    """Q = 0 and no temporal term: every logit is its bias, so per row
+    Z = n_other + sum_i n_i * prod_j g_j,i ** m_j,q, LSE = ln Z and the mass on
+    picture i is n_i * prod_j g_j,i ** m_j,q / Z (counts from the layout)."""
+    rng = np.random.default_rng(13)
+    lay = ti.make_layout(3, (2, 3), (2, 3), 3, 5, 4, mask=True)
+    planes = _two_plane_mask(lay, rng)
+    g = ((1.7, 0.6, 1.2), (0.8, 2.2, 0.9))
+    n = lay.n
+    q = np.zeros((n, 8))
+    k = rng.standard_normal((n, 8))
+    v = np.zeros((n, 3))
+    for i in range(3):
+        v[lay.picture == i, i] = 1.0
+    p = ti.Params(strength=0.0, binding=True, gains=g[0], chained=(g[1],))
+    o, l = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, planes, p)
+    counts = [int(np.sum((lay.seg == ti.SEG_PICTURE) & (lay.picture == i))) for i in range(3)]
+    n_other = n - sum(counts)
+    for r in range(n):
+        if lay.seg[r] == ti.SEG_TARGET:
+            w = [counts[i] * (g[0][i] ** float(planes[0, r])) * (g[1][i] ** float(planes[1, r])) for i in range(3)]
+        else:
+            w = [float(c) for c in counts]
+        z = n_other + sum(w)
+        assert abs(l[r] - math.log(z)) < 1e-13
+        for i in range(3):
+            assert abs(o[r, i] - w[i] / z) < 1e-13
+
+
+def test_p11_binding_order_and_bruteforce():
+    rng = np.random.default_rng(14)
+    for trial in range(4):
+        n = int(rng.integers(4, 20))
+        lay = ti.random_layout(rng, n, frames=4, pictures=3, mask=True)
+        planes = _two_plane_mask(lay, rng)
+        p = ti.random_params(rng, 3, binding=True)
+        g2 = tuple(float(x) for x in rng.uniform(0.3, 2.5, size=3))
+        q, k, v = (rng.standard_normal((n, 5)) for _ in range(3))
+        pa = ti.Params(p.window, p.falloff, p.strength, p.cap, True, p.gains, (g2,))
+        pb = ti.Params(p.window, p.falloff, p.strength, p.cap, True, g2, (tuple(p.gains),))
+        oa, la = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, planes, pa)
+        ob, lb = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, planes[::-1].copy(), pb)
+        assert np.max(np.abs(oa - ob)) < 1e-13 and np.max(np.abs(la - lb)) < 1e-13
+        bo, bl = oracle.attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), lay.seg, lay.time,
+                                             lay.picture, planes, pa)
+        assert np.max(np.abs(oa - bo)) < 1e-12 and np.max(np.abs(la - bl)) < 1e-12
+
+
 # ----------------------------------------------------- planted mistakes fail a pin
 def _pins_pass(golden_dir):
     fx = _load_penalty_fixture(golden_dir)
@@ -368,7 +456,8 @@ def _pins_pass(golden_dir):
               lambda: test_p4_q0_closed_form(fx, "binding"),
               lambda: test_p5_gain_power_m_multiplies_unnormalised_weight(),
               lambda: test_p6_bruteforce(1),
-              lambda: test_p7_partition_merge_identity(0)]
+              lambda: test_p7_partition_merge_identity(0),
+              lambda: test_p11_q0_closed_form_two_bindings()]
     for c in checks:
         try:
             c()
@@ -404,8 +493,24 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
     def transposed_kv(q, k, v, *a, **kw):
         return real_head(q, v, k, *a, **kw) if q.shape == v.shape else real_head(q, k, v, *a, **kw)
 
+    def first_binding_only(seg_q, tq, mq, seg_k, tk, pk, params):
+        # chained bindings dropped, the first mask plane kept
+        first = ti.Params(params.window, params.falloff, params.strength, params.cap, params.binding,
+                          params.gains)
+        planes = None if mq is None else np.asarray(mq).reshape(getattr(params, "num_bindings", 1), -1)
+        return real_bias(seg_q, tq, None if planes is None else planes[0], seg_k, tk, pk, first)
+
+    def one_mask_plane(seg_q, tq, mq, seg_k, tk, pk, params):
+        # every binding weighted by the first binding's mask
+        nb = getattr(params, "num_bindings", 1)
+        if mq is None or nb == 1:
+            return real_bias(seg_q, tq, mq, seg_k, tk, pk, params)
+        planes = np.asarray(mq).reshape(nb, -1)
+        return real_bias(seg_q, tq, np.stack([planes[0]] * nb), seg_k, tk, pk, params)
+
     mutants = [("penalty", no_square), ("penalty", no_window), ("bias_block", wrong_sign),
-               ("bias_block", swap_qk_roles), ("bias_block", log2_gain), ("attention_head", transposed_kv)]
+               ("bias_block", swap_qk_roles), ("bias_block", log2_gain), ("attention_head", transposed_kv),
+               ("bias_block", first_binding_only), ("bias_block", one_mask_plane)]
     for name, fn in mutants:
         with monkeypatch.context() as m:
             m.setattr(tor, name, fn)
