@@ -13,7 +13,8 @@
  *
  * and, with reference binding on ("BFS H3 Reference Attention Binding
  * (Experimental)", section "The exact rule"), logits from target queries with
- * mask weight m to keys of Picture i gain m * ln(gain_i). Every other logit is
+ * mask weight m to keys of Picture i gain m * ln(gain_i); chained bindings add
+ * their terms (section "Common issues"): sum_j m_j * ln(gain_j,i). Every other logit is
  * plain (Q . K) * softmax_scale. One non-causal softmax runs over all keys of
  * the sequence. The library returns O and the natural-log log-sum-exp (LSE) of
  * each query row's final logits.
@@ -77,6 +78,7 @@ typedef enum {
 } tara_status_t;
 
 #define TARA_MAX_PICTURES 16
+#define TARA_MAX_BINDINGS 4
 #define TARA_MAX_PARTITIONS 64
 
 /* Controls of one call. Start from tara_params_default().
@@ -84,12 +86,16 @@ typedef enum {
  *    defaults 0.20 s, 0.25 s, 2.0, 6.0). Valid: finite, window >= 0,
  *    falloff > 0, strength >= 0, cap >= 0. strength == 0 or cap == 0 removes
  *    the temporal bias (plain attention on those edges).
- *  binding_enabled, num_pictures, picture_gain: reference binding ("Inputs
- *    you'll set": picture_index chooses the Picture whose gain is
- *    reference_strength, the other pictures get other_reference_strength;
- *    1 is neutral). Here the gain is given per 0-based picture id,
- *    0 <= id < num_pictures <= TARA_MAX_PICTURES; every gain must be finite
- *    and > 0. binding_enabled == 0 ignores picture_id, mask_weight and gains.
+ *  binding_enabled, num_pictures, num_bindings, picture_gain: reference
+ *    binding ("Inputs you'll set": picture_index chooses the Picture whose
+ *    gain is reference_strength, the other pictures get
+ *    other_reference_strength; 1 is neutral). Here the gain is given per
+ *    0-based picture id, 0 <= id < num_pictures <= TARA_MAX_PICTURES.
+ *    num_bindings (1 .. TARA_MAX_BINDINGS; 0 is read as 1) bindings apply
+ *    together, as chained binding nodes do ("Common issues": their log gains
+ *    add): binding j uses picture_gain[j][*] and mask plane j. Every gain
+ *    used must be finite and > 0. binding_enabled == 0 ignores picture_id,
+ *    mask_weight and the gains.
  *  softmax_scale: multiplies Q . K only; 0 selects 1/sqrt(D).
  *  mode, num_partitions, partition_bounds: see tara_mode_t. partition_bounds
  *    is a host array of num_partitions + 1 non-decreasing key offsets from 0 to
@@ -102,7 +108,8 @@ typedef struct {
   float cap;
   int binding_enabled;
   int num_pictures;
-  float picture_gain[TARA_MAX_PICTURES];
+  int num_bindings;
+  float picture_gain[TARA_MAX_BINDINGS][TARA_MAX_PICTURES];
   float softmax_scale;
   int mode;
   int num_partitions;
@@ -110,11 +117,13 @@ typedef struct {
 } tara_params_t;
 
 /* Fills *p with the defaults: window 0.20, falloff 0.25, strength 2.0,
- * cap 6.0, binding off (all gains 1), scale 1/sqrt(D), fused mode. */
+ * cap 6.0, binding off (one binding, all gains 1), scale 1/sqrt(D), fused
+ * mode. */
 void tara_params_default(tara_params_t* p);
 
 /* Device workspace tara_attn_fwd needs for this call shape (bytes, a multiple
- * of 256). It holds per-token encodings of the metadata, per-key-tile
+ * of 256). It holds per-token encodings of the metadata (with binding, a
+ * per-query table of the summed log gains of every picture), per-key-tile
  * summaries, V laid out key-contiguous per (batch, head, dim) for the bf16
  * path, and per-partition O/LSE in partitioned mode. Returns 0 for an empty
  * call (B, H or N == 0) and (size_t)-1 for arguments tara_attn_fwd would reject
@@ -137,8 +146,9 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
  *           only for TARGET and GUIDE tokens (others may hold anything).
  *  picture_id device int16 [B][N], 0-based picture id of PICTURE tokens; read
  *           only when binding is active; may be NULL when it is not.
- *  mask_weight device fp32 [B][N] mask weight m of TARGET queries, or NULL for
- *           m = 1 everywhere ("no mask means the whole output video").
+ *  mask_weight device fp32 [num_bindings][B][N] mask weight m of TARGET
+ *           queries, one plane per binding, or NULL for m = 1 everywhere
+ *           ("no mask means the whole output video").
  *  p        host, the controls (see tara_params_t).
  *  workspace device, >= tara_workspace_bytes(...) bytes, 256-byte aligned;
  *           contents on entry are ignored, on exit unspecified.

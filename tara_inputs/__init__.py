@@ -118,12 +118,14 @@ def mask_blob(frames: int, rows: int, cols: int, seed: int = 5000, sub: int = 8)
 
 def make_layout(frames: int, target_hw: tuple, guide_hw: tuple, pictures: int,
                 picture_tokens: int, text: int, mask: bool = False,
-                mask_seed: int = 5000) -> Layout:
+                mask_seed: int = 5000, mask_planes: int = 1) -> Layout:
     """Packed sequence [target | guide | pictures by id | text], frame-major.
 
     target_hw / guide_hw are the (rows, cols) patch grid per latent frame;
     both clips cover the same latent frames. With mask=True every target
-    token gets the blob weight of its patch (others get 0).
+    token gets the blob weight of its patch (others get 0); mask_planes > 1
+    gives one plane per chained binding, plane j drawn with seed mask_seed + j
+    (the mask is then [mask_planes, N]).
     """
     tr, tc = target_hw
     gr, gc = guide_hw
@@ -145,9 +147,11 @@ def make_layout(frames: int, target_hw: tuple, guide_hw: tuple, pictures: int,
     time[vid] = frame_time(frame[vid])
     m = None
     if mask:
-        blob = mask_blob(frames, tr, tc, seed=mask_seed)
-        m = np.zeros(n, np.float32)
-        m[:nt] = blob.reshape(-1)
+        m = np.zeros((mask_planes, n), np.float32)
+        for j in range(mask_planes):
+            m[j, :nt] = mask_blob(frames, tr, tc, seed=mask_seed + j).reshape(-1)
+        if mask_planes == 1:
+            m = m[0]
     return Layout(seg, time, pic, frame, m)
 
 
@@ -174,10 +178,10 @@ class Config:
         return 1000 * self.cid + head
 
 
-def _cfg(cid, name, heads, d, dtype, frames, thw, ghw, pics, ptok, text, params, mask=False):
+def _cfg(cid, name, heads, d, dtype, frames, thw, ghw, pics, ptok, text, params, mask=False, planes=1):
     return Config(cid, name, heads, d, dtype,
                   dict(frames=frames, target_hw=thw, guide_hw=ghw, pictures=pics,
-                       picture_tokens=ptok, text=text, mask=mask), params)
+                       picture_tokens=ptok, text=text, mask=mask, mask_planes=planes), params)
 
 
 # The five workloads: 1 = tiny fp32; 2 = 54,272 tokens x 8 heads; 3 = 107,126 tokens
@@ -194,11 +198,16 @@ _CONFIGS = {
             Params(window=0.10, falloff=0.40, strength=3.0, cap=8.0, binding=True,
                    gains=(1.25, 0.75, 0.75)), mask=True),
     6: _cfg(3, "bf16-107126tok-56h-d128", 56, 128, "bf16", 107, (17, 29), (17, 29), 2, 556, 512, Params()),
+    # 5's sequence with a second, chained binding (its own mask blob and gains)
+    7: _cfg(5, "bf16-107682tok-56h-d128-chained2", 56, 128, "bf16", 107, (17, 29), (17, 29), 3, 556, 512,
+            Params(window=0.10, falloff=0.40, strength=3.0, cap=8.0, binding=True,
+                   gains=(1.25, 0.75, 0.75), chained=((0.8, 1.4, 1.1),)), mask=True, planes=2),
 }
 
 
 def config(cid: int) -> Config:
-    """Workload by id (1..5; 6 = the 107,126-token layout at 56 heads)."""
+    """Workload by id (1..5; 6 = the 107,126-token layout at 56 heads; 7 = 5
+    with a second chained binding)."""
     return _CONFIGS[cid]
 
 

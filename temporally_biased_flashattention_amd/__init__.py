@@ -11,7 +11,8 @@ References", section "The temporal rule"; "BFS H3 Reference Attention Binding
 (Experimental)", section "The exact rule"): softmax attention over a packed
 sequence where target-query x guide-key logits lose
 min(strength*(max(|t_q - t_k| - window, 0)/falloff)^2, cap) and, with binding,
-target-query x picture-key logits gain m*ln(gain).
+target-query x picture-key logits gain m*ln(gain) (chained bindings add their
+terms, section "Common issues").
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ TARA_SEG_TARGET, TARA_SEG_GUIDE, TARA_SEG_PICTURE, TARA_SEG_OTHER = 0, 1, 2, 3
 TARA_BF16, TARA_FP32 = 0, 1
 TARA_MODE_FUSED, TARA_MODE_PARTITIONED = 0, 1
 TARA_MAX_PICTURES = 16
+TARA_MAX_BINDINGS = 4
 TARA_MAX_PARTITIONS = 64
 
 EXPORTED_SYMBOLS = (
@@ -66,7 +68,8 @@ class TaraParams(ctypes.Structure):
         ("cap", ctypes.c_float),
         ("binding_enabled", ctypes.c_int),
         ("num_pictures", ctypes.c_int),
-        ("picture_gain", ctypes.c_float * TARA_MAX_PICTURES),
+        ("num_bindings", ctypes.c_int),
+        ("picture_gain", (ctypes.c_float * TARA_MAX_PICTURES) * TARA_MAX_BINDINGS),
         ("softmax_scale", ctypes.c_float),
         ("mode", ctypes.c_int),
         ("num_partitions", ctypes.c_int),
@@ -130,16 +133,24 @@ def tara_params_default() -> TaraParams:
 def make_params(window: float = 0.20, falloff: float = 0.25, strength: float = 2.0, cap: float = 6.0,
                 binding: bool = False, gains: Sequence[float] = (), softmax_scale: float = 0.0,
                 mode: str = "fused", partitions: int = 1,
-                bounds: Optional[Sequence[int]] = None) -> TaraParams:
-    """Builds tara_params_t. gains[i] is the gain of 0-based picture id i."""
+                bounds: Optional[Sequence[int]] = None,
+                chained: Sequence[Sequence[float]] = ()) -> TaraParams:
+    """Builds tara_params_t. gains[i] is the gain of 0-based picture id i
+    under the first binding; chained[j][i] that under binding j + 1."""
     p = tara_params_default()
     p.window, p.falloff, p.strength, p.cap = window, falloff, strength, cap
     p.binding_enabled = int(bool(binding))
     p.num_pictures = len(gains)
     if len(gains) > TARA_MAX_PICTURES:
         raise ValueError("at most 16 pictures")
-    for i, g in enumerate(gains):
-        p.picture_gain[i] = g
+    if 1 + len(chained) > TARA_MAX_BINDINGS:
+        raise ValueError("at most 4 bindings")
+    p.num_bindings = 1 + len(chained)
+    for j, gs in enumerate((tuple(gains),) + tuple(tuple(c) for c in chained)):
+        if len(gs) != len(gains):
+            raise ValueError("every binding gives one gain per picture")
+        for i, g in enumerate(gs):
+            p.picture_gain[j][i] = g
     p.softmax_scale = softmax_scale
     p.mode = {"fused": TARA_MODE_FUSED, "partitioned": TARA_MODE_PARTITIONED}[mode]
     p.num_partitions = int(partitions)
@@ -190,7 +201,8 @@ def tara_attn_fwd(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight
 
     q, k, v, o: [B, H, N, D] (any strides with a contiguous last dim);
     lse: fp32 [B, H, N] contiguous; seg_type uint8 [B, N]; token_time fp32
-    [B, N]; picture_id int16 [B, N] or None; mask_weight fp32 [B, N] or None;
+    [B, N]; picture_id int16 [B, N] or None; mask_weight fp32 [B, N] (one
+    binding), [J, B, N] (J chained bindings, contiguous) or None;
     workspace: a byte tensor of at least tara_workspace_bytes(...) bytes.
     stream: a torch.cuda.Stream (default: the current stream).
     """

@@ -34,15 +34,21 @@ bool env_flag(const char* name) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tq, mq, tk, kb, ksum, vt, kmax, opart, lsepart, total;
+  size_t tq, tk, kp, gt, ksum, vt, kmax, opart, lsepart, total;
 };
 
 int npad_of(int N) { return (N + tara::kBlockK - 1) / tara::kBlockK * tara::kBlockK; }
 
 int num_parts(const tara_params_t* p) { return p->mode == TARA_MODE_PARTITIONED ? p->num_partitions : 1; }
 
-// Workspace regions, each 256-byte aligned: per-token encodings, key-tile
-// summaries, V^T (bf16 path), and per-partition O/LSE (partitioned mode).
+int num_bindings(const tara_params_t* p) { return p->num_bindings < 1 ? 1 : p->num_bindings; }
+
+// Pictures of the gain table (0 without binding).
+int table_pictures(const tara_params_t* p) { return p->binding_enabled ? p->num_pictures : 0; }
+
+// Workspace regions, each 256-byte aligned: per-token encodings (with
+// binding, the per-query gain table), key-tile summaries, V^T (bf16 path),
+// and per-partition O/LSE (partitioned mode).
 WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
   WsLayout L{};
   const size_t npad = (size_t)npad_of(N), nkt = npad / tara::kBlockK;
@@ -53,9 +59,9 @@ WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tar
     return at;
   };
   L.tq = take((size_t)B * N * 4);
-  L.mq = take((size_t)B * N * 4);
   L.tk = take((size_t)B * npad * 4);
-  L.kb = take((size_t)B * npad * 4);
+  L.kp = take((size_t)B * npad * 4);
+  L.gt = take((size_t)B * N * table_pictures(p) * 4);
   L.ksum = take((size_t)B * nkt * sizeof(tara::KeyTileSummary));
   L.vt = dtype == TARA_BF16 ? take((size_t)B * H * D * npad * 2) : 0;
   L.kmax = dtype == TARA_BF16 ? take((size_t)B * H * nkt * 4) : 0;
@@ -82,9 +88,12 @@ int check_params(const tara_params_t* p, int N) {
   if (p->binding_enabled) {
     if (p->num_pictures < 0 || p->num_pictures > TARA_MAX_PICTURES)
       return fail(TARA_ERR_BAD_PARAM, "num_pictures must be in [0, 16]");
-    for (int i = 0; i < p->num_pictures; ++i)
-      if (!finite(p->picture_gain[i]) || !(p->picture_gain[i] > 0.0f))
-        return fail(TARA_ERR_BAD_PARAM, "picture gains must be finite and > 0 (the rule adds m*ln(gain))");
+    if (p->num_bindings < 0 || p->num_bindings > TARA_MAX_BINDINGS)
+      return fail(TARA_ERR_BAD_PARAM, "num_bindings must be in [0, 4] (0 is read as 1)");
+    for (int j = 0; j < num_bindings(p); ++j)
+      for (int i = 0; i < p->num_pictures; ++i)
+        if (!finite(p->picture_gain[j][i]) || !(p->picture_gain[j][i] > 0.0f))
+          return fail(TARA_ERR_BAD_PARAM, "picture gains must be finite and > 0 (the rule adds m*ln(gain))");
   }
   if (p->mode != TARA_MODE_FUSED && p->mode != TARA_MODE_PARTITIONED)
     return fail(TARA_ERR_BAD_PARAM, "mode must be TARA_MODE_FUSED or TARA_MODE_PARTITIONED");
@@ -132,9 +141,10 @@ int validate_metadata(int B, int N, const uint8_t* seg, const float* time, const
     if (hipMemcpy(hp.data(), pic, n * 2, hipMemcpyDeviceToHost) != hipSuccess)
       return fail(TARA_ERR_HIP, "TARA_VALIDATE: copying picture ids failed");
   }
+  const int nb = num_bindings(p);
   if (bind && mask) {
-    hm.resize(n);
-    if (hipMemcpy(hm.data(), mask, n * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    hm.resize(n * nb);
+    if (hipMemcpy(hm.data(), mask, n * nb * 4, hipMemcpyDeviceToHost) != hipSuccess)
       return fail(TARA_ERR_HIP, "TARA_VALIDATE: copying the mask failed");
   }
   for (size_t i = 0; i < n; ++i) {
@@ -143,8 +153,11 @@ int validate_metadata(int B, int N, const uint8_t* seg, const float* time, const
       return fail(TARA_ERR_BAD_METADATA, "token_time[" + std::to_string(i) + "] of a video token is not finite");
     if (bind && hs[i] == TARA_SEG_PICTURE && !hp.empty() && (hp[i] < 0 || hp[i] >= p->num_pictures))
       return fail(TARA_ERR_BAD_METADATA, "picture_id[" + std::to_string(i) + "] outside [0, num_pictures)");
-    if (bind && hs[i] == TARA_SEG_TARGET && !hm.empty() && !std::isfinite(hm[i]))
-      return fail(TARA_ERR_BAD_METADATA, "mask_weight[" + std::to_string(i) + "] is not finite");
+    if (bind && hs[i] == TARA_SEG_TARGET && !hm.empty())
+      for (int j = 0; j < nb; ++j)
+        if (!std::isfinite(hm[(size_t)j * n + i]))
+          return fail(TARA_ERR_BAD_METADATA, "mask_weight[" + std::to_string(j) + "][" + std::to_string(i) +
+                                                 "] is not finite");
   }
   return TARA_OK;
 }
@@ -167,7 +180,9 @@ void tara_params_default(tara_params_t* p) {
   p->cap = 6.0f;
   p->binding_enabled = 0;
   p->num_pictures = 0;
-  for (int i = 0; i < TARA_MAX_PICTURES; ++i) p->picture_gain[i] = 1.0f;
+  p->num_bindings = 1;
+  for (int j = 0; j < TARA_MAX_BINDINGS; ++j)
+    for (int i = 0; i < TARA_MAX_PICTURES; ++i) p->picture_gain[j][i] = 1.0f;
   p->softmax_scale = 0.0f;
   p->mode = TARA_MODE_FUSED;
   p->num_partitions = 1;
@@ -270,9 +285,11 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   const double log2e = 1.4426950408889634;
   const double scale = p->softmax_scale > 0.0f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)D);
   const bool bias_active = p->strength > 0.0f && p->cap > 0.0f;
+  const int nbind = num_bindings(p);
   bool binding_active = false;
   if (p->binding_enabled)
-    for (int i = 0; i < p->num_pictures; ++i) binding_active |= p->picture_gain[i] != 1.0f;
+    for (int j = 0; j < nbind; ++j)
+      for (int i = 0; i < p->num_pictures; ++i) binding_active |= p->picture_gain[j][i] != 1.0f;
   if (binding_active && !picture_id)
     return fail(TARA_ERR_NULL_POINTER, "picture_id must be non-NULL when binding is active");
 
@@ -300,13 +317,16 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   ma.nkt = nkt;
   ma.bias_active = bias_active;
   ma.binding_active = binding_active;
-  ma.num_pictures = p->binding_enabled ? p->num_pictures : 0;
-  for (int i = 0; i < tara::kMaxPictures; ++i)
-    ma.lg2gain[i] = (binding_active && i < p->num_pictures) ? (float)std::log2((double)p->picture_gain[i]) : 0.0f;
+  ma.num_pictures = table_pictures(p);
+  ma.nbind = nbind;
+  for (int j = 0; j < tara::kMaxBindings; ++j)
+    for (int i = 0; i < tara::kMaxPictures; ++i)
+      ma.lg2gain[j][i] = (binding_active && j < nbind && i < p->num_pictures)
+                             ? (float)std::log2((double)p->picture_gain[j][i]) : 0.0f;
   ma.tq = reinterpret_cast<float*>(ws + L.tq);
-  ma.mq = reinterpret_cast<float*>(ws + L.mq);
   ma.tk = reinterpret_cast<float*>(ws + L.tk);
-  ma.kb = reinterpret_cast<float*>(ws + L.kb);
+  ma.kp = reinterpret_cast<int*>(ws + L.kp);
+  ma.gt = reinterpret_cast<float*>(ws + L.gt);
   ma.ksum = reinterpret_cast<tara::KeyTileSummary*>(ws + L.ksum);
 
   tara::AttnArgs aa{};
@@ -328,9 +348,10 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   aa.npad = npad;
   aa.nkt = nkt;
   aa.tq = ma.tq;
-  aa.mq = ma.mq;
   aa.tk = ma.tk;
-  aa.kb = ma.kb;
+  aa.kp = ma.kp;
+  aa.gt = ma.gt;
+  aa.npics = ma.num_pictures;
   aa.ksum = ma.ksum;
   aa.kmax = dtype == TARA_BF16 ? reinterpret_cast<const float*>(ws + L.kmax) : nullptr;
   aa.c = (float)(scale * log2e);

@@ -10,19 +10,23 @@ namespace tara {
 constexpr int kBlockK = 64;          // keys per key tile (all paths)
 constexpr int kMaxParts = 64;        // == TARA_MAX_PARTITIONS
 constexpr int kMaxPictures = 16;     // == TARA_MAX_PICTURES
+constexpr int kMaxBindings = 4;      // == TARA_MAX_BINDINGS
 
 // Kind of a key tile, from the per-key encodings (see MetaArgs):
 //  PLAIN   no key of the tile can carry a bias term
 //  GUIDE   every key is a biased guide key; lo/hi = min/max time (s)
-//  PICTURE every key is a picture key with the same log2 gain `bias`
+//  PICTURE every key is a key of the same bound picture `pic`: the bias of a
+//          row is its gain-table entry for that picture
 //  MIXED   anything else (per-element bias)
-enum : int { KT_PLAIN = 0, KT_GUIDE = 1, KT_PICTURE = 2, KT_MIXED = 3 };
+// KT_HAS_PICTURE is or-ed into kind when some key of the tile is a bound
+// picture key (the per-element path then reads the gain table).
+enum : int { KT_PLAIN = 0, KT_GUIDE = 1, KT_PICTURE = 2, KT_MIXED = 3, KT_CLASS = 3, KT_HAS_PICTURE = 4 };
 
 struct __attribute__((aligned(16))) KeyTileSummary {
   int kind;
   float lo;
   float hi;
-  float bias;
+  int pic;      // picture id of a PICTURE tile, else -1
 };
 
 // Per-token encodings written by the metadata kernel. The temporal rule is
@@ -31,23 +35,24 @@ struct __attribute__((aligned(16))) KeyTileSummary {
 // w = window * sigma, cap2 = cap * log2 e. Times stay in seconds so the gap
 // |tq - tk| is rounded relative to itself, not to the absolute times.
 //   tq[b][n]  time of a biased (target) query, NaN otherwise
-//   mq[b][n]  mask weight m of a target query when binding is active, else 0
 //   tk[b][n]  time of a biased (guide) key, NaN otherwise (n < npad)
-//   kb[b][n]  log2 gain of a bound picture key, else 0 (n < npad)
+//   kp[b][n]  picture id of a bound picture key, -1 otherwise (n < npad)
+//   gt[b][n][P]  summed log2 gains of a target query for each picture id,
+//             sum_j m_j * log2 gain_j,p (0 for other queries); P = npics
 // A NaN time makes the penalty 0 (fmaxf(NaN, 0) = 0), which is how unbiased
 // query/key pairs drop out of the per-element formula.
 struct MetaArgs {
   const uint8_t* seg;
   const float* time;
   const int16_t* pic;
-  const float* mask;
+  const float* mask;       // [nbind][B][N] or NULL
   int B, N, npad, nkt;
-  int bias_active, binding_active, num_pictures;
-  float lg2gain[kMaxPictures];
+  int bias_active, binding_active, num_pictures, nbind;
+  float lg2gain[kMaxBindings][kMaxPictures];
   float* tq;
-  float* mq;
   float* tk;
-  float* kb;
+  int* kp;
+  float* gt;              // [B][N][num_pictures] (binding active only)
   KeyTileSummary* ksum;   // [B][nkt]
 };
 
@@ -66,9 +71,10 @@ struct AttnArgs {
   float* lsepart;          // partitioned: LSE_p [P][B][H][N]
   int B, H, N, npad, nkt, nqb;
   const float* tq;
-  const float* mq;
   const float* tk;
-  const float* kb;
+  const int* kp;
+  const float* gt;
+  int npics;               // row length of gt
   const KeyTileSummary* ksum;
   const float* kmax;       // bf16 path: [B*H][nkt] max |k| per key tile
   float c;                 // softmax_scale * log2 e

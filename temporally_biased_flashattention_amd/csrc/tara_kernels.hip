@@ -84,6 +84,7 @@ __global__ __launch_bounds__(64) void meta_kernel(MetaArgs a) {
   const int n = blockIdx.x * kBlockK + threadIdx.x;
   const bool valid = n < a.N;
   const int64_t mi = (int64_t)b * a.N + n;
+  const int64_t plane = (int64_t)a.B * a.N;   // mask plane stride
   int seg = valid ? (int)a.seg[mi] : 3;
   const float t = valid ? a.time[mi] : 0.0f;
   const bool tfinite = valid && isfinite(t);
@@ -93,28 +94,48 @@ __global__ __launch_bounds__(64) void meta_kernel(MetaArgs a) {
   if (valid) {
     const bool tgt = seg == 0;
     a.tq[mi] = (tgt && a.bias_active && tfinite) ? t : nanv;
-    float m = 0.0f;
-    if (tgt && a.binding_active) m = a.mask ? a.mask[mi] : 1.0f;
-    a.mq[mi] = m;
+    const bool bq = tgt && a.binding_active;
+    // summed log2 gains of this query for every picture: sum_j m_j * log2 gain_j,p
+    if (a.num_pictures > 0) {
+      float m[kMaxBindings];
+#pragma unroll
+      for (int j = 0; j < kMaxBindings; ++j)
+        m[j] = (bq && j < a.nbind) ? (a.mask ? a.mask[j * plane + mi] : 1.0f) : 0.0f;
+      float* g = a.gt + mi * a.num_pictures;
+      for (int p = 0; p < a.num_pictures; ++p) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kMaxBindings; ++j)
+          if (j < a.nbind) acc = fmaf(m[j], a.lg2gain[j][p], acc);
+        g[p] = acc;
+      }
+    }
   }
   // key side (n < npad)
   const bool isg = valid && seg == 1 && a.bias_active && tfinite;
   const float tk = isg ? t : nanv;
-  float kbv = 0.0f;
+  int kp = -1;
   if (valid && seg == 2 && a.binding_active) {
     const int id = a.pic[mi];
-    if (id >= 0 && id < a.num_pictures) kbv = a.lg2gain[id];
+    if (id >= 0 && id < a.num_pictures) {
+      bool live = false;   // some binding has a non-neutral gain for this picture
+#pragma unroll
+      for (int j = 0; j < kMaxBindings; ++j) live |= j < a.nbind && a.lg2gain[j][id] != 0.0f;
+      if (live) kp = id;
+    }
   }
   const int64_t ki = (int64_t)b * a.npad + n;
   a.tk[ki] = tk;
-  a.kb[ki] = kbv;
+  a.kp[ki] = kp;
 
   // tile summary
-  const bool isp = kbv != 0.0f;
+  const bool isp = kp >= 0;
   const bool all_plain = !wave_any(isg || isp);
   const bool all_guide = !wave_any(!isg);
-  const float kb0 = __shfl(kbv, 0);
-  const bool all_pic = !wave_any(!isp || kbv != kb0);
+  const int kp0 = __shfl(kp, 0);
+  // one bound picture: the bias of a row is its gain-table entry
+  const bool all_pic = !wave_any(!isp || kp != kp0);
+  const bool any_pic = wave_any(isp);
   float lo = isg ? tk : INFINITY, hi = isg ? tk : -INFINITY;
   for (int off = 32; off >= 1; off >>= 1) {
     lo = fminf(lo, __shfl_xor(lo, off));
@@ -122,10 +143,11 @@ __global__ __launch_bounds__(64) void meta_kernel(MetaArgs a) {
   }
   if (threadIdx.x == 0) {
     KeyTileSummary s;
-    s.kind = all_plain ? KT_PLAIN : all_guide ? KT_GUIDE : all_pic ? KT_PICTURE : KT_MIXED;
+    s.kind = (all_plain ? KT_PLAIN : all_guide ? KT_GUIDE : all_pic ? KT_PICTURE : KT_MIXED) |
+             (any_pic ? KT_HAS_PICTURE : 0);
     s.lo = lo;
     s.hi = hi;
-    s.bias = all_pic ? kb0 : 0.0f;
+    s.pic = all_pic ? kp0 : -1;
     a.ksum[(int64_t)b * a.nkt + blockIdx.x] = s;
   }
 }
@@ -231,6 +253,9 @@ hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, flo
 // latency is exposed where a phase starts. Between the phases every wave
 // waits for its own DMAs of K_{t+2} and V_{t+1}, and the workgroup meets at
 // its one barrier per tile.
+
+// Row pitch (floats) of the gain table copy in LDS: 16 pictures + 1 pad.
+constexpr int kGtPitch = kMaxPictures + 1;
 
 // LDS ring depth of the bf16 kernel (K and V^T tiles).
 constexpr int kStages = 3;
@@ -363,7 +388,7 @@ __device__ __forceinline__ KeyTileSummary load_summary(KsumConstPtr p, int i) {
   r.kind = p[i].kind;
   r.lo = p[i].lo;
   r.hi = p[i].hi;
-  r.bias = p[i].bias;
+  r.pic = p[i].pic;
   return r;
 }
 
@@ -371,11 +396,12 @@ __device__ __forceinline__ KeyTileSummary load_summary(KsumConstPtr p, int i) {
 // needs the per-element formula for this row; otherwise *brow is the row's
 // constant bias over the tile (log2 units).
 __device__ __forceinline__ bool tile_class_lane(const KeyTileSummary& sm, bool partial, bool qbiased, float tq,
-                                                float mq, const AttnArgs& a, float* brow) {
+                                                float gpic, const AttnArgs& a, float* brow) {
   float b = 0.0f;
   bool lane_elem = partial;
   if (!partial) {
-    if (sm.kind == KT_GUIDE) {
+    const int kind = sm.kind & KT_CLASS;
+    if (kind == KT_GUIDE) {
       if (qbiased) {
         const float dlo = sm.lo - tq, dhi = tq - sm.hi;
         const float dmin = fmaxf(fmaxf(dlo, dhi), 0.0f);
@@ -383,9 +409,9 @@ __device__ __forceinline__ bool tile_class_lane(const KeyTileSummary& sm, bool p
         if (dmin >= a.dsat) b = -a.cap2;
         else if (!(dmax <= a.window)) lane_elem = true;
       }
-    } else if (sm.kind == KT_PICTURE) {
-      b = mq * sm.bias;
-    } else if (sm.kind == KT_MIXED) {
+    } else if (kind == KT_PICTURE) {
+      b = gpic;
+    } else if (kind == KT_MIXED) {
       lane_elem = true;
     }
   }
@@ -393,11 +419,14 @@ __device__ __forceinline__ bool tile_class_lane(const KeyTileSummary& sm, bool p
   return lane_elem;
 }
 
-// Per-element bias of a key tile, in place: x = s*c + m*log2(gain) - penalty,
-// keys outside [k0, k1) -> -inf. Lane half hh holds keys 8*hh..8*hh+7 and
+// Per-element bias of a key tile, in place: x = s*c - penalty + binding, keys
+// outside [k0, k1) -> -inf. binding is the query's summed log2 gain of the
+// key's picture (gtq: this row of the gain table, in LDS; read only when the
+// tile holds bound picture keys). Lane half hh holds keys 8*hh..8*hh+7 and
 // 16+8*hh..16+8*hh+7 of each 32-key block.
-__device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, float tq, float mq, bool partial, int k0,
-                                          int k1, const float* tkb, const float* kbb, const AttnArgs& a) {
+__device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, float tq, bool has_pic,
+                                          const float* gtq, bool partial, int k0, int k1, const float* tkb,
+                                          const int* kpb, const AttnArgs& a) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -405,19 +434,35 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
       const int kx = kbase + kb * 32 + c2 * 16 + hh * 8;
       const f32x4 t0 = *reinterpret_cast<const f32x4*>(tkb + kx);
       const f32x4 t1 = *reinterpret_cast<const f32x4*>(tkb + kx + 4);
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(kbb + kx);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(kbb + kx + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float tk = e < 4 ? t0[e] : t1[e - 4];
-        const float gk = e < 4 ? g0[e] : g1[e - 4];
         const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);   // NaN time -> 0
-        const float pen = fminf(dd * dd, a.cap2);
-        float x = fmaf(s[kb][c2 * 8 + e], a.c, fmaf(mq, gk, -pen));
-        if (partial && (kx + e < k0 || kx + e >= k1)) x = -INFINITY;
-        s[kb][c2 * 8 + e] = x;
+        s[kb][c2 * 8 + e] = fmaf(s[kb][c2 * 8 + e], a.c, -fminf(dd * dd, a.cap2));
       }
     }
+  }
+  if (has_pic) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int kx = kbase + kb * 32 + (c4 >> 1) * 16 + hh * 8 + (c4 & 1) * 4;
+        const int4 pk = *reinterpret_cast<const int4*>(kpb + kx);
+        const int pe[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (pe[e] >= 0) s[kb][c4 * 4 + e] += gtq[pe[e]];
+      }
+  }
+  if (partial) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
+        if (key < k0 || key >= k1) s[kb][r] = -INFINITY;
+      }
   }
 }
 
@@ -437,7 +482,12 @@ void attn_bf16_kernel(AttnArgs a) {
   // LDS ring of NS stages: K tiles in slots 0..NS-1, then V^T tiles in slots 0..NS-1
   constexpr int NS = kStages;
   static_assert(NS == 3, "slot arithmetic and the DMA wait count assume three stages");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[NS * (KTILE + VTILE)];
+  // one LDS array (the K/V^T ring, then the workgroup's rows of the gain
+  // table with row pitch kGtPitch floats): with a second array the compiler
+  // can no longer tell the ring's DMA writes from other LDS reads and waits
+  // for every DMA before each fragment read
+  __shared__ __attribute__((aligned(16))) __bf16 smem[NS * (KTILE + VTILE) + BQ * kGtPitch * 2];
+  float* const gt_lds = reinterpret_cast<float*>(smem + NS * (KTILE + VTILE));
 #define KBUF(i) (smem + (i) * KTILE)
 #define VBUF(i) (smem + NS * KTILE + (i) * VTILE)
 
@@ -461,8 +511,14 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
   }
   const float tq = a.tq[(int64_t)b * N + qr];
-  const float mq = a.mq[(int64_t)b * N + qr];
   const bool qbiased = tq == tq;
+  // this row of the gain table into LDS (entry 0 is 0 when there is no table)
+  const float* gtq = gt_lds + (wave * 32 + lq) * kGtPitch;
+  if (hh == 0) {
+    const float* g = a.gt + ((int64_t)b * N + qr) * a.npics;
+    for (int p = 0; p < (a.npics > 0 ? a.npics : 1); ++p)
+      gt_lds[(wave * 32 + lq) * kGtPitch + p] = p < a.npics ? g[p] : 0.0f;
+  }
 
   const int k0 = a.kr[part], k1 = a.kr[part + 1];
   if (k1 <= k0) {
@@ -515,7 +571,7 @@ void attn_bf16_kernel(AttnArgs a) {
   };
 
   const float* tkb = a.tk + (int64_t)b * a.npad;
-  const float* kbb = a.kb + (int64_t)b * a.npad;
+  const int* kpb = a.kp + (int64_t)b * a.npad;
   // tile summaries and key norms through the constant address space: uniform
   // loads of them become scalar loads
   const KsumConstPtr ks_c = (KsumConstPtr)(a.ksum + (int64_t)b * a.nkt);
@@ -563,11 +619,12 @@ void attn_bf16_kernel(AttnArgs a) {
     const int kbase = kt0 * kBlockK;
     const bool partial = kbase < k0 || kbase + kBlockK > k1;
     const KeyTileSummary sm0 = load_summary(ks_c, kt0);
+    const float gpic0 = gtq[max(sm0.pic, 0)];
     float brow;
-    const bool lane_elem = tile_class_lane(sm0, partial, qbiased, tq, mq, a, &brow);
+    const bool lane_elem = tile_class_lane(sm0, partial, qbiased, tq, gpic0, a, &brow);
     float cc = a.c;
     if (wave_any(lane_elem)) {
-      elem_bias(x, kbase, hh, tq, mq, partial, k0, k1, tkb, kbb, a);
+      elem_bias(x, kbase, hh, tq, (sm0.kind & KT_HAS_PICTURE) != 0, gtq, partial, k0, k1, tkb, kpb, a);
       brow = 0.0f;
       cc = 1.0f;
     }
@@ -590,7 +647,7 @@ void attn_bf16_kernel(AttnArgs a) {
     fr[2] = kfrag<KROW>(kr0, 2);
     // every wave is done with K slot 0 before iteration t0 restages it
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.bias), "s"(kmax_next));
+    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next));
   }
 
   // ring slots at iteration t: K_t, V_t in s0; K_{t+1}, V_{t+1} in s1; K_{t+2}
@@ -602,11 +659,14 @@ void attn_bf16_kernel(AttnArgs a) {
     const bool has1 = t + 1 < kt1;
     const int s1 = s0 + 1 == NS ? 0 : s0 + 1;
     const int s2 = s1 + 1 == NS ? 0 : s1 + 1;
+    const KeyTileSummary sm1 = sm_next;
+    const float kmax1 = kmax_next;
+    // a one-picture tile's bias is this row's gain-table entry for the
+    // picture (read every tile, so no path waits on a pending load)
+    const float gpic1 = gtq[max(sm1.pic, 0)];
     stage_k(t + NS, s0);
     const int kbase1 = (t + 1) * kBlockK;
     const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
-    const KeyTileSummary sm1 = sm_next;
-    const float kmax1 = kmax_next;
     const __bf16* kr0 = KBUF(s1) + koff_lane;   // K_{t+1}
     const __bf16* vr0 = VBUF(s0) + voff_lane;   // V_t
     const __bf16* kn0 = KBUF(s2) + koff_lane;   // K_{t+2}
@@ -645,9 +705,9 @@ void attn_bf16_kernel(AttnArgs a) {
     float cc = a.c;
     bool need_max = false;
     if (has1) {
-      const bool lane_elem = tile_class_lane(sm1, partial1, qbiased, tq, mq, a, &brow);
+      const bool lane_elem = tile_class_lane(sm1, partial1, qbiased, tq, gpic1, a, &brow);
       if (wave_any(lane_elem)) {
-        elem_bias(sn, kbase1, hh, tq, mq, partial1, k0, k1, tkb, kbb, a);
+        elem_bias(sn, kbase1, hh, tq, (sm1.kind & KT_HAS_PICTURE) != 0, gtq, partial1, k0, k1, tkb, kpb, a);
         brow = 0.0f;
         cc = 1.0f;
         need_max = true;
@@ -678,7 +738,7 @@ void attn_bf16_kernel(AttnArgs a) {
     sm_next = load_summary(ks_c, min(t + 2, kt1 - 1));
     kmax_next = kmax_c[min(t + 2, kt1 - 1)];
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.bias), "s"(kmax_next));
+    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next));
     stage_v(t + NS - 1, s2);
 
     // phase B: O^T += V_t^T P_t^T | row sum of P_t, X_{t+1} = S_{t+1} c +
@@ -804,9 +864,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     ov[i] = ov[i + 1] = ov[i + 2] = ov[i + 3] = 0.0f;
   }
   const float tq = a.tq[(int64_t)b * N + qr];
-  const float mq = a.mq[(int64_t)b * N + qr];
   const float* tkb = a.tk + (int64_t)b * a.npad;
-  const float* kbb = a.kb + (int64_t)b * a.npad;
+  const int* kpb = a.kp + (int64_t)b * a.npad;
+  const float* gtq = a.gt + ((int64_t)b * N + qr) * a.npics;
   const int k0 = a.kr[part], k1 = a.kr[part + 1];
   float m = -INFINITY, l = 0.0f;
   for (int kx = k0; kx < k1; ++kx) {
@@ -823,7 +883,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     sdot += __shfl_xor(sdot, 1);
     sdot += __shfl_xor(sdot, 2);
     const float dd = fmaxf(fmaf(fabsf(tq - tkb[kx]), a.sigma, -a.w), 0.0f);
-    const float x = fmaf(sdot, a.c, fmaf(mq, kbb[kx], -fminf(dd * dd, a.cap2)));
+    const int pk = kpb[kx];
+    const float x = fmaf(sdot, a.c, (pk >= 0 ? gtq[pk] : 0.0f) - fminf(dd * dd, a.cap2));
     const float mn = fmaxf(m, x);
     const float alpha = exp2f(m - mn);
     const float p = exp2f(x - mn);

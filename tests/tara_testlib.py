@@ -32,14 +32,16 @@ def log(msg: str):
 def tara_params(p: ti.Params, mode="fused", partitions=1, bounds=None, softmax_scale=0.0):
     return tara.make_params(window=p.window, falloff=p.falloff, strength=p.strength, cap=p.cap,
                             binding=p.binding, gains=tuple(p.gains), softmax_scale=softmax_scale,
-                            mode=mode, partitions=partitions, bounds=bounds)
+                            mode=mode, partitions=partitions, bounds=bounds,
+                            chained=tuple(tuple(c) for c in p.chained))
 
 
 def device_meta(lay: ti.Layout, device="cuda", batch=1):
-    """Metadata tensors [batch, N] on the device (the same layout per batch element)."""
+    """Metadata tensors [batch, N] on the device (the same layout per batch
+    element); a mask with one plane per binding becomes [J, batch, N]."""
     def rep(x, dt):
         t = torch.from_numpy(np.ascontiguousarray(x)).to(dt)
-        return t.unsqueeze(0).repeat(batch, 1).to(device)
+        return t.unsqueeze(-2).repeat(*([1] * (t.dim() - 1)), batch, 1).contiguous().to(device)
     seg = rep(lay.seg, torch.uint8)
     tim = rep(lay.time, torch.float32)
     pic = rep(lay.picture, torch.int16)

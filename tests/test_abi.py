@@ -36,10 +36,11 @@ def test_params_struct_matches_header_defaults():
     p = tara.tara_params_default()
     assert (p.window, p.falloff, p.strength, p.cap) == pytest.approx((0.20, 0.25, 2.0, 6.0))
     assert p.binding_enabled == 0 and p.mode == tara.TARA_MODE_FUSED and p.num_partitions == 1
-    assert all(p.picture_gain[i] == 1.0 for i in range(16))
+    assert p.num_bindings == 1
+    assert all(p.picture_gain[j][i] == 1.0 for j in range(4) for i in range(16))
     assert p.softmax_scale == 0.0
-    # ctypes layout: 4 floats, 2 ints, 16 floats, float, 2 ints, pointer
-    assert ctypes.sizeof(tara.TaraParams) == 4 * 4 + 2 * 4 + 16 * 4 + 4 + 2 * 4 + 4 + 8
+    # ctypes layout: 4 floats, 3 ints, 4x16 floats, float, 2 ints, pointer
+    assert ctypes.sizeof(tara.TaraParams) == 4 * 4 + 3 * 4 + 64 * 4 + 4 + 2 * 4 + 8
 
 
 def _al(x):
@@ -51,13 +52,15 @@ def test_workspace_bytes():
     B, H, N, D = 1, 2, 1000, 128
     npad = 1024
     nkt = npad // 64
-    meta = 2 * _al(B * N * 4) + 2 * _al(B * npad * 4) + _al(B * nkt * 16)
+    meta = _al(B * N * 4) + 2 * _al(B * npad * 4) + _al(0) + _al(B * nkt * 16)
     bf16_extra = _al(B * H * D * npad * 2) + _al(B * H * nkt * 4)     # V^T, per-tile max |k|
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p) == meta + bf16_extra
     assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, p) == meta
     pp = tara.make_params(mode="partitioned", partitions=3)
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, pp) == (
         meta + bf16_extra + _al(3 * B * H * N * D * 4) + _al(3 * B * H * N * 4))
+    pb = tara.make_params(binding=True, gains=(1.25, 0.75, 0.75), chained=((0.9, 1.1, 1.0),))
+    assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, pb) == meta + _al(B * N * 3 * 4)   # gain table
     assert tara.tara_workspace_bytes(tara.TARA_BF16, 0, H, N, D, p) == 0
     with pytest.raises(tara.TaraError):
         tara.tara_workspace_bytes(tara.TARA_BF16, 1, 1, 10, 96, p)
@@ -104,6 +107,13 @@ def test_rejections(lib):
     assert call(lib, tara.make_params(binding=True, gains=(1.25, 0.0))) == -6
     assert call(lib, tara.make_params(binding=True, gains=(1.25, -2.0))) == -6
     assert call(lib, tara.make_params(softmax_scale=-1.0)) == -6
+    assert call(lib, tara.make_params(binding=True, gains=(1.25, 0.5), chained=((1.0, 0.0),))) == -6
+    assert call(lib, tara.make_params(binding=True, gains=(1.25, 0.5), chained=((1.0, float("nan")),))) == -6
+    pb = tara.make_params(binding=True, gains=(1.25,))
+    pb.num_bindings = 5
+    assert call(lib, pb) == -6
+    pb.num_bindings = -1
+    assert call(lib, pb) == -6
     assert call(lib, tara.make_params(binding=True, gains=(1.25,)), pic=0) == -1   # ids needed
     assert call(lib, tara.make_params(mode="partitioned", partitions=0)) == -6
     assert call(lib, tara.make_params(mode="partitioned", partitions=65)) == -6
