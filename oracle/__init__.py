@@ -5,4 +5,4 @@ import this package; the product library never does.
 """
 from .tara_oracle import (TARGET, GUIDE, PICTURE, OTHER, penalty, saturation_gap,  # noqa: F401
                           bias_block, attention_head, attention, merge_partitions,
-                          attention_bruteforce, flops)
+                          attention_bruteforce, three_term_parts, flops)

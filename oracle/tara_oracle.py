@@ -180,6 +180,65 @@ def merge_partitions(parts) -> Tuple[np.ndarray, np.ndarray]:
     return o, lse
 
 
+# -------------------------------------------------------- three-term partitions
+def three_term_parts(q, k, v, seg, time, picture, mask, params, rows=None, scale=None):
+    """The three non-negative contributions of the Flash Partitions backend.
+
+    "TARA: Native Temporal Alignment for MiniMax H3 References", section
+    "Three backends": the rule is evaluated by FlashAttention with LSE outputs,
+    merging three non-negative contributions instead of building a dense bias
+    tensor. Reading (section "The temporal rule": the penalty reaches cap at
+    the saturation gap and stays there): with G the guide keys (empty when the
+    temporal bias is off, strength or cap 0),
+      A: keys outside G, with their normal logits (binding term included);
+      B: keys in G, every target row at -cap (other rows unbiased);
+      C: keys in G for target rows, weight e^s (e^-penalty - e^-cap) >= 0,
+         zero past the saturation gap.
+    Returns [(O_A, LSE_A), (O_B, LSE_B), (O_C, LSE_C)] in fp64 (an empty term
+    has LSE -inf and O 0); merge_partitions of them is attention_head.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    seg = np.asarray(seg)
+    tm = np.asarray(time, np.float64)
+    bias_on = params.strength > 0.0 and params.cap > 0.0
+    g = (seg == GUIDE) if bias_on else np.zeros(n, bool)
+    s = (q[rows] @ k.T) * sc
+    full = s + bias_block(seg[rows], tm[rows], None if mask is None else np.asarray(mask)[..., rows],
+                          seg, tm, np.asarray(picture), params)
+    tgt = seg[rows] == TARGET
+
+    def softmax_part(z):
+        # rows with no finite logit give an empty term
+        o = np.zeros((rows.size, v.shape[1]))
+        lse = np.full(rows.size, -np.inf)
+        zmax = z.max(axis=1)
+        ok = np.isfinite(zmax)
+        if ok.any():
+            zz = z[ok] - zmax[ok, None]
+            l = np.log(np.exp(zz).sum(axis=1)) + zmax[ok]
+            w = np.exp(z[ok] - l[:, None])
+            o[ok] = w @ v
+            lse[ok] = l
+        return o, lse
+
+    za = np.where(g[None, :], -np.inf, full)
+    zb = np.where(g[None, :], s - np.where(tgt, params.cap, 0.0)[:, None], -np.inf)
+    # term C as a logit: s + ln(e^-p - e^-cap) on (target row, guide key) pairs
+    pen = np.zeros_like(s)
+    if g.any():
+        pen[:, g] = penalty(tm[rows][:, None] - tm[g][None, :], params.window, params.falloff,
+                            params.strength, params.cap)
+    with np.errstate(divide="ignore"):
+        corr = np.log(np.maximum(np.exp(-pen) - math.exp(-params.cap), 0.0))
+    zc = np.where(g[None, :] & tgt[:, None], s + corr, -np.inf)
+    return [softmax_part(za), softmax_part(zb), softmax_part(zc)]
+
+
 # -------------------------------------------------------------------- brute force
 def attention_bruteforce(q, k, v, seg, time, picture, mask, params, scale=None):
     """Pure-Python loops with exactly rounded sums, for tiny inputs (N <= ~32).

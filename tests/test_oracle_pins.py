@@ -304,6 +304,44 @@ def test_p8_three_nonnegative_terms():
         assert abs(math.log(t1 + t2 + t3) - lse[i]) < 1e-12
 
 
+@pytest.mark.parametrize("case", ["defaults", "binding", "strength0", "shuffled"])
+def test_p8_three_term_parts_merge_to_attention(case):
+    """The three terms as LSE partitions (unbiased/binding keys; guide keys at
+    -cap; local correction) merge exactly into the full result, row by row,
+    and every target row's correction term vanishes past the saturation gap."""
+    rng = np.random.default_rng(91)
+    lay = ti.make_layout(8, (3, 3), (3, 3), 2, 7, 5, mask=True)
+    if case == "shuffled":
+        lay = lay.permuted(rng.permutation(lay.n))
+    n, d = lay.n, 16
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    p = {"defaults": DEFAULTS, "binding": BIND5, "strength0": ti.Params(strength=0.0),
+         "shuffled": BIND5}[case]
+    parts = oracle.three_term_parts(q, k, v, lay.seg, lay.time, lay.picture, lay.mask, p)
+    o, l = oracle.attention_head(q, k, v, lay.seg, lay.time, lay.picture, lay.mask, p)
+    om, lm = oracle.merge_partitions(parts)
+    assert np.max(np.abs(om - o)) < 1e-12 and np.max(np.abs(lm - l)) < 1e-12
+    tgt = lay.seg == ti.SEG_TARGET
+    if case == "strength0":
+        assert np.all(np.isneginf(parts[1][1])) and np.all(np.isneginf(parts[2][1]))
+        return
+    # non-target rows have no correction term; B is the guide keys' plain LSE shifted by -cap on target rows
+    assert np.all(np.isneginf(parts[2][1][~tgt]))
+    g = lay.seg == ti.SEG_GUIDE
+    s = (q @ k.T) / math.sqrt(d)
+    plain_b = np.log(np.exp(s[:, g]).sum(axis=1))
+    assert np.max(np.abs(parts[1][1] - (plain_b - np.where(tgt, p.cap, 0.0)))) < 1e-12
+    # the correction of a target row only sees guide keys closer than the saturation gap
+    dsat = tor.saturation_gap(p.window, p.falloff, p.strength, p.cap)
+    for i in np.nonzero(tgt)[0]:
+        near = g & (np.abs(lay.time.astype(np.float64) - float(lay.time[i])) < dsat)
+        pen = tor.penalty(float(lay.time[i]) - lay.time[near].astype(np.float64), p.window, p.falloff,
+                          p.strength, p.cap)
+        w = np.exp(s[i, near]) * (np.exp(-pen) - math.exp(-p.cap))
+        want = math.log(w.sum()) if w.sum() > 0 else -math.inf
+        assert abs(parts[2][1][i] - want) < 1e-12 or (want == -math.inf and parts[2][1][i] == -math.inf)
+
+
 # ----------------------------------------------------------- P9: invariances
 def test_p9_invariances():
     rng = np.random.default_rng(21)
@@ -457,7 +495,8 @@ def _pins_pass(golden_dir):
               lambda: test_p5_gain_power_m_multiplies_unnormalised_weight(),
               lambda: test_p6_bruteforce(1),
               lambda: test_p7_partition_merge_identity(0),
-              lambda: test_p11_q0_closed_form_two_bindings()]
+              lambda: test_p11_q0_closed_form_two_bindings(),
+              lambda: test_p8_three_term_parts_merge_to_attention("defaults")]
     for c in checks:
         try:
             c()
@@ -508,12 +547,32 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
         planes = np.asarray(mq).reshape(nb, -1)
         return real_bias(seg_q, tq, np.stack([planes[0]] * nb), seg_k, tk, pk, params)
 
+    real_three = tor.three_term_parts
+
+    def correction_keeps_cap(*a, **kw):
+        # local correction without subtracting the cap contribution (counts it twice)
+        parts = real_three(*a, **kw)
+        q, k, v, seg, time, picture, mask, params = a[:8]
+        s = np.asarray(q, np.float64) @ np.asarray(k, np.float64).T / math.sqrt(np.asarray(q).shape[1])
+        g = np.asarray(seg) == tor.GUIDE
+        tgt = np.asarray(seg) == tor.TARGET
+        pen = np.zeros_like(s)
+        tm = np.asarray(time, np.float64)
+        pen[:, g] = tor.penalty(tm[:, None] - tm[g][None, :], params.window, params.falloff, params.strength,
+                                params.cap)
+        zc = np.where(g[None, :] & tgt[:, None], s - pen, -np.inf)
+        l = np.full(s.shape[0], -np.inf)
+        ok = tgt & g.any()
+        l[ok] = np.log(np.exp(zc[ok]).sum(axis=1))
+        return [parts[0], parts[1], (parts[2][0], l)]
+
     mutants = [("penalty", no_square), ("penalty", no_window), ("bias_block", wrong_sign),
                ("bias_block", swap_qk_roles), ("bias_block", log2_gain), ("attention_head", transposed_kv),
-               ("bias_block", first_binding_only), ("bias_block", one_mask_plane)]
+               ("bias_block", first_binding_only), ("bias_block", one_mask_plane),
+               ("three_term_parts", correction_keeps_cap)]
     for name, fn in mutants:
         with monkeypatch.context() as m:
             m.setattr(tor, name, fn)
-            if name == "attention_head":
-                m.setattr(oracle, "attention_head", fn)
+            if name in ("attention_head", "three_term_parts"):
+                m.setattr(oracle, name, fn)
             assert not _pins_pass(golden_dir), f"planted mistake {fn.__name__} went unnoticed"
