@@ -61,8 +61,17 @@ typedef enum { TARA_BF16 = 0, TARA_FP32 = 1 } tara_dtype_t;
  * PARTITIONED: the keys are split into num_partitions contiguous ranges, each
  * range is attended on its own with its own LSE, and the ranges are merged
  * exactly by log-sum-exp (the LSE-merging evaluation of the "Three backends"
- * section). Both modes return the same O and LSE up to rounding. */
-typedef enum { TARA_MODE_FUSED = 0, TARA_MODE_PARTITIONED = 1 } tara_mode_t;
+ * section).
+ * THREE_TERM: the Flash Partitions evaluation of that section, read as three
+ * non-negative contributions, each attended as its own LSE partition and then
+ * merged exactly: (A) keys that are not temporally biased guide keys, normal
+ * logits; (B) the biased guide keys with every target row at -cap; (C) the
+ * local correction e^s (e^-penalty - e^-cap) of target rows over guide keys
+ * closer than the saturation gap window + falloff*sqrt(cap/strength). Each
+ * pass visits only the key tiles holding keys of its term. N <= 2^20;
+ * num_partitions and partition_bounds are ignored.
+ * All modes return the same O and LSE up to rounding. */
+typedef enum { TARA_MODE_FUSED = 0, TARA_MODE_PARTITIONED = 1, TARA_MODE_THREE_TERM = 2 } tara_mode_t;
 
 typedef enum {
   TARA_OK = 0,
@@ -125,7 +134,7 @@ void tara_params_default(tara_params_t* p);
  * of 256). It holds per-token encodings of the metadata (with binding, a
  * per-query table of the summed log gains of every picture), per-key-tile
  * summaries, V laid out key-contiguous per (batch, head, dim) for the bf16
- * path, and per-partition O/LSE in partitioned mode. Returns 0 for an empty
+ * path, and per-partition O/LSE in the partitioned and three-term modes. Returns 0 for an empty
  * call (B, H or N == 0) and (size_t)-1 for arguments tara_attn_fwd would reject
  * (p == NULL, bad dtype or head dim, bad partition count). */
 size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,

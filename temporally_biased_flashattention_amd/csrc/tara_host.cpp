@@ -39,7 +39,11 @@ struct WsLayout {
 
 int npad_of(int N) { return (N + tara::kBlockK - 1) / tara::kBlockK * tara::kBlockK; }
 
-int num_parts(const tara_params_t* p) { return p->mode == TARA_MODE_PARTITIONED ? p->num_partitions : 1; }
+int num_parts(const tara_params_t* p) {
+  return p->mode == TARA_MODE_PARTITIONED ? p->num_partitions : p->mode == TARA_MODE_THREE_TERM ? 3 : 1;
+}
+
+bool has_partials(const tara_params_t* p) { return p->mode != TARA_MODE_FUSED; }
 
 int num_bindings(const tara_params_t* p) { return p->num_bindings < 1 ? 1 : p->num_bindings; }
 
@@ -65,8 +69,8 @@ WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tar
   L.ksum = take((size_t)B * nkt * sizeof(tara::KeyTileSummary));
   L.vt = dtype == TARA_BF16 ? take((size_t)B * H * D * npad * 2) : 0;
   L.kmax = dtype == TARA_BF16 ? take((size_t)B * H * nkt * 4) : 0;
-  if (p->mode == TARA_MODE_PARTITIONED) {
-    const size_t parts = (size_t)p->num_partitions;
+  if (has_partials(p)) {
+    const size_t parts = (size_t)num_parts(p);
     L.opart = take(parts * B * H * N * D * 4);
     L.lsepart = take(parts * B * H * N * 4);
   }
@@ -95,8 +99,8 @@ int check_params(const tara_params_t* p, int N) {
         if (!finite(p->picture_gain[j][i]) || !(p->picture_gain[j][i] > 0.0f))
           return fail(TARA_ERR_BAD_PARAM, "picture gains must be finite and > 0 (the rule adds m*ln(gain))");
   }
-  if (p->mode != TARA_MODE_FUSED && p->mode != TARA_MODE_PARTITIONED)
-    return fail(TARA_ERR_BAD_PARAM, "mode must be TARA_MODE_FUSED or TARA_MODE_PARTITIONED");
+  if (p->mode != TARA_MODE_FUSED && p->mode != TARA_MODE_PARTITIONED && p->mode != TARA_MODE_THREE_TERM)
+    return fail(TARA_ERR_BAD_PARAM, "mode must be TARA_MODE_FUSED, TARA_MODE_PARTITIONED or TARA_MODE_THREE_TERM");
   if (p->mode == TARA_MODE_PARTITIONED) {
     if (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS)
       return fail(TARA_ERR_BAD_PARAM, "num_partitions must be in [1, 64]");
@@ -261,6 +265,8 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (B < 0 || H < 0 || N < 0) return fail(TARA_ERR_BAD_SHAPE, "B, H and N must be >= 0");
   if ((int64_t)B * H > 65535) return fail(TARA_ERR_BAD_SHAPE, "B * H must be <= 65535");
   if (N > (1 << 30)) return fail(TARA_ERR_BAD_SHAPE, "N must be <= 2^30");
+  if (p && p->mode == TARA_MODE_THREE_TERM && npad_of(N) / tara::kBlockK > tara::kMaxListTiles)
+    return fail(TARA_ERR_BAD_SHAPE, "three-term mode supports N <= 2^20 (its key-tile lists live in LDS)");
   if (int st = check_params(p, N)) return st;
   if (B == 0 || H == 0 || N == 0) {
     g_info = tara_run_info_t{p->mode, (int)dtype, 0, 0, num_parts(p), 0, tara::kBlockK, 0, 0};
@@ -340,8 +346,9 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   aa.o_sb = o_str[0]; aa.o_sh = o_str[1]; aa.o_sn = o_str[2];
   aa.o = o;
   aa.lse = lse;
-  aa.opart = p->mode == TARA_MODE_PARTITIONED ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
-  aa.lsepart = p->mode == TARA_MODE_PARTITIONED ? reinterpret_cast<float*>(ws + L.lsepart) : nullptr;
+  // per-partition outputs: every mode but fused (range partitions, the three terms)
+  aa.opart = has_partials(p) ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
+  aa.lsepart = has_partials(p) ? reinterpret_cast<float*>(ws + L.lsepart) : nullptr;
   aa.B = B;
   aa.H = H;
   aa.N = N;
@@ -362,13 +369,20 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   aa.window = p->window;
   aa.dsat = bias_active ? (float)((double)p->window + (double)p->falloff * std::sqrt((double)p->cap / (double)p->strength))
                         : INFINITY;
+  aa.corr0 = bias_active ? (float)std::log2(-std::expm1(-(double)p->cap)) : -INFINITY;
   aa.nparts = parts;
   if (p->mode == TARA_MODE_PARTITIONED && p->partition_bounds) {
     for (int i = 0; i <= parts; ++i) aa.kr[i] = p->partition_bounds[i];
   } else {
     for (int i = 0; i <= parts; ++i) aa.kr[i] = (int)((int64_t)N * i / parts);
   }
-  const bool partitioned = p->mode == TARA_MODE_PARTITIONED;
+  const bool partitioned = has_partials(p);
+  // passes of the attention kernel: one fused pass, one pass over all key
+  // ranges, or the three terms
+  std::vector<int> passes;
+  if (p->mode == TARA_MODE_FUSED) passes = {tara::PASS_FUSED};
+  else if (p->mode == TARA_MODE_PARTITIONED) passes = {tara::PASS_RANGE};
+  else passes = {tara::PASS_TERM_A, tara::PASS_TERM_B, tara::PASS_TERM_C};
   int launches = 0;
   hipError_t e = tara::launch_meta(ma, stream);
   ++launches;
@@ -394,18 +408,24 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     }
   }
   int grid = 0, block_q = 0;
-  if (dtype == TARA_BF16) {
-    aa.nqb = (N + tara::attn_bf16_block_q(D) - 1) / tara::attn_bf16_block_q(D);
-    block_q = tara::attn_bf16_block_q(D);
-    grid = tara::attn_bf16_grid(aa) * (partitioned ? parts : 1);
-    e = tara::launch_attn_bf16(aa, D, partitioned, stream);
-  } else {
-    block_q = tara::attn_f32_block_q(D);
-    aa.nqb = (N + block_q - 1) / block_q;
-    grid = aa.nqb * B * H * (partitioned ? parts : 1);
-    e = tara::launch_attn_f32(aa, D, partitioned, stream);
+  for (int pass : passes)
+    if (pass != tara::PASS_FUSED && (!aa.opart || !aa.lsepart))
+      return fail(TARA_ERR_HIP, "internal: a partition pass without its partial-output buffers");
+  for (int pass : passes) {
+    if (dtype == TARA_BF16) {
+      block_q = tara::attn_bf16_block_q(D);
+      aa.nqb = (N + block_q - 1) / block_q;
+      grid += tara::attn_bf16_grid(aa) * (pass == tara::PASS_RANGE ? parts : 1);
+      e = tara::launch_attn_bf16(aa, D, pass, stream);
+    } else {
+      block_q = tara::attn_f32_block_q(D);
+      aa.nqb = (N + block_q - 1) / block_q;
+      grid += aa.nqb * B * H * (pass == tara::PASS_RANGE ? parts : 1);
+      e = tara::launch_attn_f32(aa, D, pass, stream);
+    }
+    ++launches;
+    if (e != hipSuccess) break;
   }
-  ++launches;
   if (ev1) {
     std::lock_guard<std::mutex> lk(g_tmu);
     (void)hipEventRecord(ev1, stream);
@@ -429,7 +449,8 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   g_info_valid = true;
   if (env_flag("TARA_LOG"))
     std::fprintf(stderr, "[tara] %s %s B=%d H=%d N=%d D=%d bias=%d binding=%d parts=%d grid=%d launches=%d\n",
-                 partitioned ? "partitioned" : "fused", dtype == TARA_BF16 ? "bf16" : "fp32", B, H, N, D,
+                 p->mode == TARA_MODE_THREE_TERM ? "three-term" : partitioned ? "partitioned" : "fused",
+                 dtype == TARA_BF16 ? "bf16" : "fp32", B, H, N, D,
                  (int)bias_active, (int)binding_active, parts, grid, launches);
   return TARA_OK;
 }

@@ -11,6 +11,20 @@ constexpr int kBlockK = 64;          // keys per key tile (all paths)
 constexpr int kMaxParts = 64;        // == TARA_MAX_PARTITIONS
 constexpr int kMaxPictures = 16;     // == TARA_MAX_PICTURES
 constexpr int kMaxBindings = 4;      // == TARA_MAX_BINDINGS
+constexpr int kMaxListTiles = 16384; // key tiles a three-term pass can list (N <= 2^20)
+
+// What one pass of the attention kernel computes.
+//  FUSED   all keys, final O and LSE
+//  RANGE   key range [kr[p], kr[p+1]) of partition p = blockIdx.y -> O_p, LSE_p
+//  TERM_A/B/C  the three non-negative contributions of the Flash Partitions
+//          evaluation ("Three backends"), each a partition (p = 0, 1, 2):
+//          A: keys that are not biased guide keys, normal logits;
+//          B: biased guide keys, target rows at -cap (other rows unbiased);
+//          C: biased guide keys x target rows, weight e^s (e^-penalty - e^-cap),
+//             i.e. logit s + ln(e^-penalty - e^-cap) (-inf past the saturation gap).
+//          A pass visits only the key tiles that hold keys of its term (and, for
+//          C, guide times within the saturation gap of the workgroup's rows).
+enum : int { PASS_FUSED = 0, PASS_RANGE = 1, PASS_TERM_A = 2, PASS_TERM_B = 3, PASS_TERM_C = 4 };
 
 // Kind of a key tile, from the per-key encodings (see MetaArgs):
 //  PLAIN   no key of the tile can carry a bias term
@@ -83,6 +97,7 @@ struct AttnArgs {
   float cap2;              // cap * log2 e
   float window;            // seconds: gaps <= window carry no penalty
   float dsat;              // seconds: gaps >= window + falloff*sqrt(cap/strength) carry exactly cap
+  float corr0;             // log2(1 - 2^-cap2): term C's logit offset for gaps inside the window
   int nparts;
   int kr[kMaxParts + 1];   // partition key offsets (fused: {0, N})
 };
@@ -104,9 +119,9 @@ hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, flo
 // Block of query rows per workgroup of the bf16 attention kernel.
 int attn_bf16_block_q(int D);
 int attn_bf16_grid(const AttnArgs& a);
-hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool partitioned, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, hipStream_t s);
 int attn_f32_block_q(int D);
-hipError_t launch_attn_f32(const AttnArgs& a, int D, bool partitioned, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int D, int pass, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16_out, hipStream_t s);
 
 }  // namespace tara

@@ -394,39 +394,68 @@ __device__ __forceinline__ KeyTileSummary load_summary(KsumConstPtr p, int i) {
 
 // Bias class of one key tile for one query row: returns true when the tile
 // needs the per-element formula for this row; otherwise *brow is the row's
-// constant bias over the tile (log2 units).
+// constant bias over the tile (log2 units; -inf: the tile adds nothing to this
+// row's pass).
+template <int PASS>
 __device__ __forceinline__ bool tile_class_lane(const KeyTileSummary& sm, bool partial, bool qbiased, float tq,
                                                 float gpic, const AttnArgs& a, float* brow) {
   float b = 0.0f;
   bool lane_elem = partial;
   if (!partial) {
     const int kind = sm.kind & KT_CLASS;
-    if (kind == KT_GUIDE) {
-      if (qbiased) {
-        const float dlo = sm.lo - tq, dhi = tq - sm.hi;
-        const float dmin = fmaxf(fmaxf(dlo, dhi), 0.0f);
-        const float dmax = fmaxf(-dlo, -dhi);
-        if (dmin >= a.dsat) b = -a.cap2;
-        else if (!(dmax <= a.window)) lane_elem = true;
+    const float dlo = sm.lo - tq, dhi = tq - sm.hi;
+    const float dmin = fmaxf(fmaxf(dlo, dhi), 0.0f);
+    const float dmax = fmaxf(-dlo, -dhi);
+    if (PASS == PASS_TERM_A) {
+      // keys that are not biased guide keys, normal logits
+      if (kind == KT_GUIDE) b = -INFINITY;
+      else if (kind == KT_PICTURE) b = gpic;
+      else if (kind == KT_MIXED) lane_elem = true;
+    } else if (PASS == PASS_TERM_B) {
+      // biased guide keys, target rows at -cap
+      if (kind == KT_GUIDE) b = qbiased ? -a.cap2 : 0.0f;
+      else if (kind == KT_MIXED) lane_elem = true;
+      else b = -INFINITY;
+    } else if (PASS == PASS_TERM_C) {
+      // biased guide keys x target rows: s + log2(2^-penalty - 2^-cap)
+      if (kind == KT_GUIDE && qbiased) {
+        if (dmin >= a.dsat) b = -INFINITY;
+        else if (dmax <= a.window) b = a.corr0;
+        else lane_elem = true;
+      } else if (kind == KT_MIXED && qbiased) {
+        lane_elem = true;
+      } else {
+        b = -INFINITY;
       }
-    } else if (kind == KT_PICTURE) {
-      b = gpic;
-    } else if (kind == KT_MIXED) {
-      lane_elem = true;
+    } else {
+      if (kind == KT_GUIDE) {
+        if (qbiased) {
+          if (dmin >= a.dsat) b = -a.cap2;
+          else if (!(dmax <= a.window)) lane_elem = true;
+        }
+      } else if (kind == KT_PICTURE) {
+        b = gpic;
+      } else if (kind == KT_MIXED) {
+        lane_elem = true;
+      }
     }
   }
   *brow = b;
   return lane_elem;
 }
 
-// Per-element bias of a key tile, in place: x = s*c - penalty + binding, keys
-// outside [k0, k1) -> -inf. binding is the query's summed log2 gain of the
-// key's picture (gtq: this row of the gain table, in LDS; read only when the
-// tile holds bound picture keys). Lane half hh holds keys 8*hh..8*hh+7 and
-// 16+8*hh..16+8*hh+7 of each 32-key block.
+// Per-element logits of a key tile, in place (log2 units), keys outside
+// [k0, k1) -> -inf. Fused / range passes: x = s*c - penalty + binding, where
+// binding is the query's summed log2 gain of the key's picture (gtq: this row
+// of the gain table, in LDS; read only when the tile holds bound picture
+// keys). Term passes keep only their keys (see PASS_TERM_*). A key is a biased
+// guide key when its encoded time is not NaN. Lane half hh holds keys
+// 8*hh..8*hh+7 and 16+8*hh..16+8*hh+7 of each 32-key block.
+template <int PASS>
 __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, float tq, bool has_pic,
                                           const float* gtq, bool partial, int k0, int k1, const float* tkb,
                                           const int* kpb, const AttnArgs& a) {
+  const bool qb = tq == tq;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -438,11 +467,20 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
       for (int e = 0; e < 8; ++e) {
         const float tk = e < 4 ? t0[e] : t1[e - 4];
         const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);   // NaN time -> 0
-        s[kb][c2 * 8 + e] = fmaf(s[kb][c2 * 8 + e], a.c, -fminf(dd * dd, a.cap2));
+        const float pen = fminf(dd * dd, a.cap2);
+        const float sv = s[kb][c2 * 8 + e];
+        const bool isg = tk == tk;
+        float x;
+        if (PASS == PASS_TERM_A) x = isg ? -INFINITY : sv * a.c;
+        else if (PASS == PASS_TERM_B) x = isg ? fmaf(sv, a.c, qb ? -a.cap2 : 0.0f) : -INFINITY;
+        else if (PASS == PASS_TERM_C)
+          x = isg && qb ? fmaf(sv, a.c, __log2f(1.0f - fast_exp2(pen - a.cap2)) - pen) : -INFINITY;
+        else x = fmaf(sv, a.c, -pen);
+        s[kb][c2 * 8 + e] = x;
       }
     }
   }
-  if (has_pic) {
+  if (has_pic && (PASS == PASS_FUSED || PASS == PASS_RANGE || PASS == PASS_TERM_A)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -466,9 +504,11 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
   }
 }
 
-template <int D, int NW, bool PART>
+template <int D, int NW, int PASS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void attn_bf16_kernel(AttnArgs a) {
+  constexpr bool PART = PASS != PASS_FUSED;   // writes one partition's (O_p, LSE_p)
+  constexpr bool TERM = PASS >= PASS_TERM_A;  // visits a listed subset of the key tiles
   constexpr int BQ = NW * 32;              // query rows per workgroup
   constexpr int KROW = D + 8;              // padded LDS pitch of a K row (elements)
   constexpr int VROW = kBlockK + 8;        // padded LDS pitch of a V^T row (elements)
@@ -483,15 +523,20 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int NS = kStages;
   static_assert(NS == 3, "slot arithmetic and the DMA wait count assume three stages");
   // one LDS array (the K/V^T ring, then the workgroup's rows of the gain
-  // table with row pitch kGtPitch floats): with a second array the compiler
-  // can no longer tell the ring's DMA writes from other LDS reads and waits
-  // for every DMA before each fragment read
-  __shared__ __attribute__((aligned(16))) __bf16 smem[NS * (KTILE + VTILE) + BQ * kGtPitch * 2];
+  // table with row pitch kGtPitch floats, then for term passes the list of
+  // key tiles to visit and a little scratch): with a second array the
+  // compiler can no longer tell the ring's DMA writes from other LDS reads and
+  // waits for every DMA before each fragment read
+  constexpr int GT_ELEMS = BQ * kGtPitch * 2;
+  constexpr int LIST_ELEMS = TERM ? kMaxListTiles + 4 * NW : 0;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[NS * (KTILE + VTILE) + GT_ELEMS + LIST_ELEMS];
   float* const gt_lds = reinterpret_cast<float*>(smem + NS * (KTILE + VTILE));
+  uint16_t* const tlist = reinterpret_cast<uint16_t*>(smem + NS * (KTILE + VTILE) + GT_ELEMS);
+  int* const tscr = reinterpret_cast<int*>(tlist + kMaxListTiles);   // 2*NW ints
 #define KBUF(i) (smem + (i) * KTILE)
 #define VBUF(i) (smem + NS * KTILE + (i) * VTILE)
 
-  const int part = PART ? blockIdx.y : 0;
+  const int part = PASS == PASS_RANGE ? blockIdx.y : TERM ? PASS - PASS_TERM_A : 0;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = L / a.nqb, qblk = L % a.nqb;
   const int b = bh / a.H, h = bh % a.H;
@@ -520,9 +565,9 @@ void attn_bf16_kernel(AttnArgs a) {
       gt_lds[(wave * 32 + lq) * kGtPitch + p] = p < a.npics ? g[p] : 0.0f;
   }
 
-  const int k0 = a.kr[part], k1 = a.kr[part + 1];
-  if (k1 <= k0) {
-    // empty key range (partitioned mode only): contributes nothing to the merge
+  const int k0 = TERM ? 0 : a.kr[part], k1 = TERM ? N : a.kr[part + 1];
+  // an empty partition contributes nothing to the merge
+  auto write_empty = [&]() {
     if (PART && qvalid) {
       float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
 #pragma unroll
@@ -531,9 +576,74 @@ void attn_bf16_kernel(AttnArgs a) {
         for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
       if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = -INFINITY;
     }
+  };
+  if (k1 <= k0) {
+    write_empty();
     return;
   }
   const int kt0 = k0 / kBlockK, kt1 = (k1 + kBlockK - 1) / kBlockK;
+
+  // tiles this pass visits: kt0 .. kt1-1, or for a term pass the listed ones
+  int ntiles = kt1 - kt0;
+  if (TERM) {
+    // times of this workgroup's biased rows
+    float tlo = qbiased && qvalid ? tq : INFINITY, thi = qbiased && qvalid ? tq : -INFINITY;
+    for (int off = 32; off >= 1; off >>= 1) {
+      tlo = fminf(tlo, __shfl_xor(tlo, off));
+      thi = fmaxf(thi, __shfl_xor(thi, off));
+    }
+    float* tsf = reinterpret_cast<float*>(tscr);
+    if (lane == 0) {
+      tsf[wave] = tlo;
+      tsf[NW + wave] = thi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      tlo = fminf(tlo, tsf[w]);
+      thi = fmaxf(thi, tsf[NW + w]);
+    }
+    __syncthreads();
+    // compact the indices of the tiles holding keys of this term
+    const KeyTileSummary* ks_g = a.ksum + (int64_t)b * a.nkt;
+    int base = 0;
+    for (int r = 0; r < a.nkt; r += NW * 64) {
+      const int i = r + tid;
+      bool keep = false;
+      if (i < a.nkt) {
+        const KeyTileSummary sm = ks_g[i];
+        const bool has_guide = sm.lo <= sm.hi;   // some biased guide key
+        if (PASS == PASS_TERM_A) keep = (sm.kind & KT_CLASS) != KT_GUIDE;
+        else if (PASS == PASS_TERM_B) keep = has_guide;
+        else keep = has_guide && tlo <= thi && fmaxf(fmaxf(sm.lo - thi, tlo - sm.hi), 0.0f) < a.dsat;
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (lane == 0) tscr[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int off = base, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = tscr[w];
+        off += w < wave ? c : 0;
+        tot += c;
+      }
+      if (keep) tlist[off + below] = (uint16_t)i;
+      __syncthreads();
+      base += tot;
+    }
+    ntiles = base;
+    if (ntiles == 0) {
+      write_empty();
+      return;
+    }
+  }
+  // key tile visited at step i (steps past the end repeat the last tile: the
+  // ring slot it is staged into is free either way)
+  auto tile_at = [&](int i) -> int {
+    if (TERM) return __builtin_amdgcn_readfirstlane((int)tlist[min(i, ntiles - 1)]);
+    return min(kt0 + i, kt1 - 1);
+  };
 
   // staging: buffer ranges over this head's K rows and V^T rows; per-lane
   // 32-bit offsets within a tile, per-tile scalar offsets
@@ -549,10 +659,8 @@ void attn_bf16_kernel(AttnArgs a) {
   VDma vdma;
   kdma.init(wave, lane, k_sn_bytes);
   vdma.init(wave, lane, (uint32_t)a.npad * 2);
-  // K tile kk into K slot sk, V^T tile kv into V slot sv; indices past the
-  // range are clamped to its last tile (the slot is free either way)
+  // K tile kk into K slot sk, V^T tile kv into V slot sv
   auto stage_k = [&](int kk, int sk) {
-    kk = min(kk, kt1 - 1);
     const int rows_left = N - kk * kBlockK;
     const uint32_t soff = (uint32_t)kk * kBlockK * k_sn_bytes;
     char* l = reinterpret_cast<char*>(KBUF(sk));
@@ -560,7 +668,6 @@ void attn_bf16_kernel(AttnArgs a) {
     else kdma.template issue<true>(rk, soff, rows_left, k_sn_bytes, l, wave);
   };
   auto stage_v = [&](int kv, int sv) {
-    kv = min(kv, kt1 - 1);
     vdma.template issue<false>(rv, (uint32_t)kv * kBlockK * 2, kBlockK, 0, reinterpret_cast<char*>(VBUF(sv)), wave);
   };
   // this wave's DMAs of K_{t+2} and V_{t+1} have landed; those of K_{t+3},
@@ -606,25 +713,27 @@ void attn_bf16_kernel(AttnArgs a) {
   const int voff_lane = lq * VROW + hh * 8;          // phase B reads V^T rows db*32 + lq
 
   {
-    // prologue: K_t0..K_t0+2 into K slots 0..2, V_t0 and V_t0+1 into V slots
-    // 0 and 1; S_t0 and X_t0; the first three K_{t0+1} fragments
-    stage_k(kt0, 0);
-    stage_k(kt0 + 1, 1);
-    stage_k(kt0 + 2, 2);
-    stage_v(kt0, 0);
-    stage_v(kt0 + 1, 1);
+    // prologue: the first three tiles' K into K slots 0..2, the first two
+    // tiles' V^T into V slots 0 and 1; S and X of the first tile; the first
+    // three K fragments of the second tile
+    const int tile0 = tile_at(0);
+    stage_k(tile0, 0);
+    stage_k(tile_at(1), 1);
+    stage_k(tile_at(2), 2);
+    stage_v(tile0, 0);
+    stage_v(tile_at(1), 1);
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
-    const int kbase = kt0 * kBlockK;
+    const int kbase = tile0 * kBlockK;
     const bool partial = kbase < k0 || kbase + kBlockK > k1;
-    const KeyTileSummary sm0 = load_summary(ks_c, kt0);
+    const KeyTileSummary sm0 = load_summary(ks_c, tile0);
     const float gpic0 = gtq[max(sm0.pic, 0)];
     float brow;
-    const bool lane_elem = tile_class_lane(sm0, partial, qbiased, tq, gpic0, a, &brow);
+    const bool lane_elem = tile_class_lane<PASS>(sm0, partial, qbiased, tq, gpic0, a, &brow);
     float cc = a.c;
     if (wave_any(lane_elem)) {
-      elem_bias(x, kbase, hh, tq, (sm0.kind & KT_HAS_PICTURE) != 0, gtq, partial, k0, k1, tkb, kpb, a);
+      elem_bias<PASS>(x, kbase, hh, tq, (sm0.kind & KT_HAS_PICTURE) != 0, gtq, partial, k0, k1, tkb, kpb, a);
       brow = 0.0f;
       cc = 1.0f;
     }
@@ -633,14 +742,15 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+    // a row with no finite logit yet keeps m = -inf; its exponent reference is 0
     m_used = fmaf(xor32_max(mx), cc, brow);
-    const float off = brow - m_used;
+    const float off = brow - (m_used == -INFINITY ? 0.0f : m_used);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(x[kb][r], cc, off);
-    sm_next = load_summary(ks_c, min(kt0 + 1, kt1 - 1));
-    kmax_next = kmax_c[min(kt0 + 1, kt1 - 1)];
+    sm_next = load_summary(ks_c, tile_at(1));
+    kmax_next = kmax_c[tile_at(1)];
     const __bf16* kr0 = KBUF(1) + koff_lane;
     fr[0] = kfrag<KROW>(kr0, 0);
     fr[1] = kfrag<KROW>(kr0, 1);
@@ -650,22 +760,27 @@ void attn_bf16_kernel(AttnArgs a) {
     asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next));
   }
 
-  // ring slots at iteration t: K_t, V_t in s0; K_{t+1}, V_{t+1} in s1; K_{t+2}
-  // and V_{t-1} in s2. K_{t+3} is staged into s0 at the start (K_t was last
-  // read before the previous barrier), V_{t+2} into s2 after this iteration's
-  // barrier (V_{t-1} was last read before it).
+  // ring slots at step t (visiting tile T_t): K and V^T of T_t in s0, of
+  // T_{t+1} in s1; K of T_{t+2} and V^T of T_{t-1} in s2. K of T_{t+3} is
+  // staged into s0 at the start (T_t's K was last read before the previous
+  // barrier), V^T of T_{t+2} into s2 after this step's barrier (T_{t-1}'s V^T
+  // was last read before it). tw1..tw3 hold T_{t+1} .. T_{t+3}; a term pass
+  // reads T_{t+4} from its LDS list one step ahead (tv4).
   int s0 = 0;
-  for (int t = kt0; t < kt1; ++t) {
-    const bool has1 = t + 1 < kt1;
+  int tw1 = tile_at(1), tw2 = tile_at(2), tw3 = tile_at(3);
+  for (int t = 0; t < ntiles; ++t) {
+    const bool has1 = t + 1 < ntiles;
     const int s1 = s0 + 1 == NS ? 0 : s0 + 1;
     const int s2 = s1 + 1 == NS ? 0 : s1 + 1;
+    int tv4 = 0;
+    if (TERM) tv4 = tlist[min(t + 4, ntiles - 1)];
     const KeyTileSummary sm1 = sm_next;
     const float kmax1 = kmax_next;
     // a one-picture tile's bias is this row's gain-table entry for the
     // picture (read every tile, so no path waits on a pending load)
     const float gpic1 = gtq[max(sm1.pic, 0)];
-    stage_k(t + NS, s0);
-    const int kbase1 = (t + 1) * kBlockK;
+    stage_k(tw3, s0);
+    const int kbase1 = tw1 * kBlockK;
     const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
     const __bf16* kr0 = KBUF(s1) + koff_lane;   // K_{t+1}
     const __bf16* vr0 = VBUF(s0) + voff_lane;   // V_t
@@ -705,9 +820,10 @@ void attn_bf16_kernel(AttnArgs a) {
     float cc = a.c;
     bool need_max = false;
     if (has1) {
-      const bool lane_elem = tile_class_lane(sm1, partial1, qbiased, tq, gpic1, a, &brow);
+      const bool lane_elem = tile_class_lane<PASS>(sm1, partial1, qbiased, tq, gpic1, a, &brow);
       if (wave_any(lane_elem)) {
-        elem_bias(sn, kbase1, hh, tq, (sm1.kind & KT_HAS_PICTURE) != 0, gtq, partial1, k0, k1, tkb, kpb, a);
+        elem_bias<PASS>(sn, kbase1, hh, tq, (sm1.kind & KT_HAS_PICTURE) != 0, gtq, partial1, k0, k1, tkb, kpb,
+                        a);
         brow = 0.0f;
         cc = 1.0f;
         need_max = true;
@@ -728,18 +844,18 @@ void attn_bf16_kernel(AttnArgs a) {
       const float mt = fmaf(xor32_max(fmaxf(mxa, mxb)), cc, brow);
       if (mt > m_used + kRescaleTau) m_new = mt;
     }
-    const float off = brow - m_new;
+    const float off = brow - (m_new == -INFINITY ? 0.0f : m_new);
 
     // K_{t+2} and V_{t+1} have landed for every wave past this barrier; the
     // scalar loads are taken right after it, where no LDS read is pending (a
     // scalar load in flight would turn the fragment waits of phase B into
     // full drains: scalar loads complete out of order)
     wait_staged();
-    sm_next = load_summary(ks_c, min(t + 2, kt1 - 1));
-    kmax_next = kmax_c[min(t + 2, kt1 - 1)];
+    sm_next = load_summary(ks_c, tw2);
+    kmax_next = kmax_c[tw2];
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next));
-    stage_v(t + NS - 1, s2);
+    stage_v(tw2, s2);
 
     // phase B: O^T += V_t^T P_t^T | row sum of P_t, X_{t+1} = S_{t+1} c +
     // brow - m_new. The ring's last three fetches are the next phase A's
@@ -771,23 +887,32 @@ void attn_bf16_kernel(AttnArgs a) {
     keep16(x[1]);
     lsum += ts0 + ts1;
     if (wave_any(m_new > m_used)) {
-      // lazy rescale after the PV product of tile t (which used the old m)
-      const float alpha = fast_exp2(m_used - m_new);
+      // lazy rescale after the PV product of tile t (which used the old m);
+      // rows whose m stays put (possibly still -inf) keep their sums as they are
+      const float alpha = m_new > m_used ? fast_exp2(m_used - m_new) : 1.0f;
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) o[i] *= alpha;
       m_used = m_new;
     }
     s0 = s1;
+    tw1 = tw2;
+    tw2 = tw3;
+    tw3 = TERM ? __builtin_amdgcn_readfirstlane(tv4) : min(kt0 + t + 4, kt1 - 1);
   }
   // no DMA may still target this workgroup's LDS when it exits
   wait_vm<0>();
 
-  // epilogue
+  // epilogue (a row without any contribution: O 0, LSE -inf)
   const float ltot = xor32_sum(lsum);
   if (!qvalid) return;
-  const float inv = 1.0f / ltot;
-  const float lse = (m_used + __log2f(ltot)) * kLn2;
+  const bool nonempty = ltot > 0.0f;
+  const float inv = nonempty ? 1.0f / ltot : 0.0f;
+  const float lse = nonempty ? (m_used + __log2f(ltot)) * kLn2 : -INFINITY;
+  if (!nonempty) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  }
   if (PART) {
     float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
 #pragma unroll
@@ -825,16 +950,22 @@ int attn_bf16_block_q(int) { return kWaves * 32; }
 
 int attn_bf16_grid(const AttnArgs& a) { return a.nqb * a.B * a.H; }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool partitioned, hipStream_t s) {
-  dim3 grid(attn_bf16_grid(a), partitioned ? a.nparts : 1);
-  dim3 block(kWaves * 64);
-  if (D == 128) {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, kWaves, false>), grid, block, 0, s, a);
-  } else {
-    if (partitioned) hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaves, false>), grid, block, 0, s, a);
+template <int D>
+void launch_attn_bf16_d(const AttnArgs& a, int pass, dim3 grid, dim3 block, hipStream_t s) {
+  switch (pass) {
+    case PASS_FUSED: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED>), grid, block, 0, s, a); break;
+    case PASS_RANGE: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE>), grid, block, 0, s, a); break;
+    case PASS_TERM_A: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_A>), grid, block, 0, s, a); break;
+    case PASS_TERM_B: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_B>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_C>), grid, block, 0, s, a); break;
   }
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, hipStream_t s) {
+  dim3 grid(attn_bf16_grid(a), pass == PASS_RANGE ? a.nparts : 1);
+  dim3 block(kWaves * 64);
+  if (D == 128) launch_attn_bf16_d<128>(a, pass, grid, block, s);
+  else launch_attn_bf16_d<64>(a, pass, grid, block, s);
   return hipGetLastError();
 }
 
@@ -843,10 +974,12 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool partitioned, hipStrea
 // keys are streamed from global memory (broadcast within the workgroup).
 constexpr int kF32Queries = 64;
 
-template <int D, bool PART>
+template <int D, int PASS>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int DL = D / 4;
-  const int part = PART ? blockIdx.z : 0;
+  constexpr bool PART = PASS != PASS_FUSED;
+  constexpr bool TERM = PASS >= PASS_TERM_A;
+  const int part = PASS == PASS_RANGE ? blockIdx.z : TERM ? PASS - PASS_TERM_A : 0;
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int N = a.N;
   const int tid = threadIdx.x, sub = tid & 3;
@@ -867,7 +1000,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const float* tkb = a.tk + (int64_t)b * a.npad;
   const int* kpb = a.kp + (int64_t)b * a.npad;
   const float* gtq = a.gt + ((int64_t)b * N + qr) * a.npics;
-  const int k0 = a.kr[part], k1 = a.kr[part + 1];
+  const int k0 = TERM ? 0 : a.kr[part], k1 = TERM ? N : a.kr[part + 1];
+  const bool qb = tq == tq;
   float m = -INFINITY, l = 0.0f;
   for (int kx = k0; kx < k1; ++kx) {
     const float* kp = kg + (int64_t)kx * a.k_sn;
@@ -882,9 +1016,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     }
     sdot += __shfl_xor(sdot, 1);
     sdot += __shfl_xor(sdot, 2);
-    const float dd = fmaxf(fmaf(fabsf(tq - tkb[kx]), a.sigma, -a.w), 0.0f);
+    const float tk = tkb[kx];
+    const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);
+    const float pen = fminf(dd * dd, a.cap2);
     const int pk = kpb[kx];
-    const float x = fmaf(sdot, a.c, (pk >= 0 ? gtq[pk] : 0.0f) - fminf(dd * dd, a.cap2));
+    const float gain = pk >= 0 ? gtq[pk] : 0.0f;
+    const bool isg = tk == tk;   // a biased guide key
+    float x;
+    if (PASS == PASS_TERM_A) x = isg ? -INFINITY : fmaf(sdot, a.c, gain);
+    else if (PASS == PASS_TERM_B) x = isg ? fmaf(sdot, a.c, qb ? -a.cap2 : 0.0f) : -INFINITY;
+    else if (PASS == PASS_TERM_C) x = isg && qb ? fmaf(sdot, a.c, __log2f(1.0f - exp2f(pen - a.cap2)) - pen) : -INFINITY;
+    else x = fmaf(sdot, a.c, gain - pen);
+    if (x == -INFINITY) continue;   // the key is outside this pass (same for the row's 4 lanes)
     const float mn = fmaxf(m, x);
     const float alpha = exp2f(m - mn);
     const float p = exp2f(x - mn);
@@ -901,7 +1044,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     m = mn;
   }
   if (!qvalid) return;
-  const bool empty = k1 <= k0;
+  const bool empty = !(l > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l;
   const float lse = empty ? -INFINITY : (m + log2f(l)) * kLn2;
   float* op;
@@ -918,16 +1061,22 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 int attn_f32_block_q(int) { return kF32Queries; }
 
-hipError_t launch_attn_f32(const AttnArgs& a, int D, bool partitioned, hipStream_t s) {
-  dim3 grid((a.N + kF32Queries - 1) / kF32Queries, a.B * a.H, partitioned ? a.nparts : 1);
-  dim3 block(256);
-  if (D == 128) {
-    if (partitioned) hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, block, 0, s, a);
-  } else {
-    if (partitioned) hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, block, 0, s, a);
+template <int D>
+void launch_attn_f32_d(const AttnArgs& a, int pass, dim3 grid, dim3 block, hipStream_t s) {
+  switch (pass) {
+    case PASS_FUSED: hipLaunchKernelGGL((attn_f32_kernel<D, PASS_FUSED>), grid, block, 0, s, a); break;
+    case PASS_RANGE: hipLaunchKernelGGL((attn_f32_kernel<D, PASS_RANGE>), grid, block, 0, s, a); break;
+    case PASS_TERM_A: hipLaunchKernelGGL((attn_f32_kernel<D, PASS_TERM_A>), grid, block, 0, s, a); break;
+    case PASS_TERM_B: hipLaunchKernelGGL((attn_f32_kernel<D, PASS_TERM_B>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_f32_kernel<D, PASS_TERM_C>), grid, block, 0, s, a); break;
   }
+}
+
+hipError_t launch_attn_f32(const AttnArgs& a, int D, int pass, hipStream_t s) {
+  dim3 grid((a.N + kF32Queries - 1) / kF32Queries, a.B * a.H, pass == PASS_RANGE ? a.nparts : 1);
+  dim3 block(256);
+  if (D == 128) launch_attn_f32_d<128>(a, pass, grid, block, s);
+  else launch_attn_f32_d<64>(a, pass, grid, block, s);
   return hipGetLastError();
 }
 

@@ -59,6 +59,9 @@ def test_workspace_bytes():
     pp = tara.make_params(mode="partitioned", partitions=3)
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, pp) == (
         meta + bf16_extra + _al(3 * B * H * N * D * 4) + _al(3 * B * H * N * 4))
+    p3 = tara.make_params(mode="three-term")
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p3) == (
+        meta + bf16_extra + _al(3 * B * H * N * D * 4) + _al(3 * B * H * N * 4))
     pb = tara.make_params(binding=True, gains=(1.25, 0.75, 0.75), chained=((0.9, 1.1, 1.0),))
     assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, pb) == meta + _al(B * N * 3 * 4)   # gain table
     assert tara.tara_workspace_bytes(tara.TARA_BF16, 0, H, N, D, p) == 0
@@ -123,6 +126,8 @@ def test_rejections(lib):
     p = P()
     p.mode = 7
     assert call(lib, p) == -6
+    # three-term passes keep their key-tile lists in LDS: N <= 2^20
+    assert call(lib, tara.make_params(mode="three-term"), N=(1 << 20) + 64, H=1) == -2
 
 
 def test_messages(lib):
