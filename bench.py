@@ -1,10 +1,12 @@
 """Throughput of TARA attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5] [--mode fused|partitioned]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5|7]
+                    [--mode fused|partitioned|three-term]
 
 A step is one tara_attn_fwd call (metadata encoding, V layout pass, the fused
-attention kernel; plus the merge in partitioned mode) over the whole workload,
-inputs already resident in HBM. The default workload is the 107,126-token
+attention kernel; in partitioned mode the range passes plus the merge; in
+three-term mode the three Flash Partitions passes plus the merge) over the
+whole workload, inputs already resident in HBM. The default workload is the 107,126-token
 packed sequence (52,751 target + 52,751 guide + 2 x 556 picture + 512 text
 tokens, 107 latent frames) at 56 heads of dim 128 in bf16 with the default
 TARA controls. Prints one JSON line.
@@ -97,7 +99,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline")
-    ap.add_argument("--mode", default="fused", choices=["fused", "partitioned"])
+    ap.add_argument("--mode", default="fused", choices=["fused", "partitioned", "three-term"])
     ap.add_argument("--partitions", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -131,11 +133,13 @@ def main():
     seg = torch.from_numpy(lay.seg)[None].to(dev)
     tim = torch.from_numpy(lay.time)[None].to(dev)
     pic = torch.from_numpy(lay.picture)[None].to(dev)
-    mask = None if lay.mask is None else torch.from_numpy(lay.mask)[None].to(dev)
+    # mask: [1, N], or [J, 1, N] with one plane per chained binding
+    mask = None if lay.mask is None else torch.from_numpy(lay.mask)[..., None, :].contiguous().to(dev)
     cp = cfg.params
     params = tara.make_params(window=cp.window, falloff=cp.falloff, strength=cp.strength, cap=cp.cap,
                               binding=cp.binding, gains=tuple(cp.gains), mode=args.mode,
-                              partitions=args.partitions if args.mode == "partitioned" else 1)
+                              partitions=args.partitions if args.mode == "partitioned" else 1,
+                              chained=tuple(tuple(c) for c in cp.chained))
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     ws = torch.empty(max(tara.tara_workspace_bytes(tara.TARA_BF16 if cfg.dtype == "bf16" else tara.TARA_FP32,
@@ -196,7 +200,8 @@ def main():
                    "mode": args.mode, "partitions": info.get("num_partitions"),
                    "controls": {"window": cfg.params.window, "falloff": cfg.params.falloff,
                                 "strength": cfg.params.strength, "cap": cfg.params.cap,
-                                "binding": cfg.params.binding, "gains": list(cfg.params.gains)},
+                                "binding": cfg.params.binding, "gains": list(cfg.params.gains),
+                                "chained_gains": [list(c) for c in cfg.params.chained]},
                    "block_q": info.get("block_q"), "block_k": info.get("block_k"), "grid": info.get("grid")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
