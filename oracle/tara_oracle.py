@@ -239,6 +239,59 @@ def three_term_parts(q, k, v, seg, time, picture, mask, params, rows=None, scale
     return [softmax_part(za), softmax_part(zb), softmax_part(zc)]
 
 
+# ------------------------------------------------------------- 8-bit Q.K (fp8)
+# The pages name a dense INT8 one-pass variant of the kernel ("Three
+# backends") but give no quantisation scheme; this is the scheme the 8-bit
+# Q.K mode uses (a reading, stated in the design notes): OCP FP8 E4M3 values,
+# round to nearest even, with a power-of-two scale per query row and per
+# 64-key tile of a head, 2^(floor(log2 max|x|) - 7), so the largest magnitude
+# lands in [128, 256). Attention then runs on the dequantised Q and K.
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_round(x):
+    """Round to the nearest FP8 E4M3 value (ties to even); |x| <= 448 expected.
+
+    E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; normals from 2^-6,
+    subnormals in steps of 2^-9. Rounding is to a multiple of the value's ulp,
+    2^(floor(log2|x|) - 3) for normals and 2^-9 below 2^-6.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value outside the E4M3 range")
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0.0, a, 1.0)))
+    ulp = 2.0 ** (np.maximum(e, -6.0) - 3.0)
+    return np.sign(x) * np.round(a / ulp) * ulp          # np.round rounds half to even
+
+
+def pow2_scale(amax: float) -> float:
+    """Power-of-two scale putting amax into [128, 256): 2^(floor(log2 amax) - 7)."""
+    if not amax > 0.0:
+        return 1.0
+    m, e = math.frexp(amax)            # amax = m * 2^e, m in [0.5, 1)
+    return math.ldexp(1.0, e - 1 - 7)
+
+
+def qk8_dequantize(q, k, tile: int = 64):
+    """Q and K as the 8-bit Q.K product sees them: each Q row and each tile of
+    `tile` consecutive K rows scaled by its power-of-two scale, rounded to
+    E4M3 and scaled back. fp64 [N, D] each."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    qd = np.empty_like(q)
+    for i in range(q.shape[0]):
+        s = pow2_scale(float(np.abs(q[i]).max()))
+        qd[i] = fp8_e4m3_round(q[i] / s) * s
+    kd = np.empty_like(k)
+    for t0 in range(0, k.shape[0], tile):
+        blk = k[t0:t0 + tile]
+        s = pow2_scale(float(np.abs(blk).max()))
+        kd[t0:t0 + tile] = fp8_e4m3_round(blk / s) * s
+    return qd, kd
+
+
 # -------------------------------------------------------------------- brute force
 def attention_bruteforce(q, k, v, seg, time, picture, mask, params, scale=None):
     """Pure-Python loops with exactly rounded sums, for tiny inputs (N <= ~32).

@@ -485,6 +485,61 @@ def test_p11_binding_order_and_bruteforce():
         assert np.max(np.abs(oa - bo)) < 1e-12 and np.max(np.abs(la - bl)) < 1e-12
 
 
+# ---------------------------------------------------- P12: 8-bit Q.K scheme
+def test_p12_fp8_e4m3_hand_worked(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "fp8_e4m3_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                a, b = line.split()
+                rows.append((float(a), float(b)))
+    assert len(rows) >= 12
+    got = oracle.fp8_e4m3_round(np.array([r[0] for r in rows]))
+    assert np.array_equal(got, np.array([r[1] for r in rows]))
+
+
+def test_p12_fp8_e4m3_against_code_table():
+    """Every E4M3 code's value rounds to itself; points between two adjacent
+    values round to the nearer one, midpoints to the one with an even code."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue                                     # NaN code
+            vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+    vals = np.array(sorted(set(vals)))                       # 0 .. 448, codes in increasing order
+    assert vals[-1] == 448.0 and len(vals) == 127
+    assert np.array_equal(oracle.fp8_e4m3_round(vals), vals)
+    assert np.array_equal(oracle.fp8_e4m3_round(-vals), -vals)
+    lo, hi = vals[:-1], vals[1:]
+    mid = (lo + hi) / 2
+    codes = np.arange(len(vals))
+    even_pick = np.where(codes[:-1] % 2 == 0, lo, hi)
+    assert np.array_equal(oracle.fp8_e4m3_round(mid), even_pick)
+    assert np.array_equal(oracle.fp8_e4m3_round(lo + (hi - lo) * 0.3), lo)
+    assert np.array_equal(oracle.fp8_e4m3_round(lo + (hi - lo) * 0.7), hi)
+
+
+def test_p12_scales_and_dequantised_error():
+    rng = np.random.default_rng(120)
+    q = rng.standard_normal((300, 64)) * np.exp(rng.uniform(-6, 6, size=(300, 1)))
+    k = rng.standard_normal((300, 64)) * 3.0
+    for row in q[:20]:
+        s = oracle.pow2_scale(float(np.abs(row).max()))
+        assert math.log2(s) == int(math.log2(s)) and 128.0 <= np.abs(row).max() / s < 256.0
+    assert oracle.pow2_scale(0.0) == 1.0
+    qd, kd = oracle.qk8_dequantize(q, k)
+    for x, xd, tile in ((q, qd, 1), (k, kd, 64)):
+        for t0 in range(0, x.shape[0], tile):
+            blk, bd = x[t0:t0 + tile], xd[t0:t0 + tile]
+            s = oracle.pow2_scale(float(np.abs(blk).max()))
+            normal = np.abs(blk) / s >= 2.0 ** -6
+            # half an ulp: 2^-4 relative for normals, 2^-10 * scale below
+            assert np.all(np.abs(bd - blk)[normal] <= np.abs(blk)[normal] * 2.0 ** -4)
+            assert np.all(np.abs(bd - blk)[~normal] <= s * 2.0 ** -10)
+
+
 # ----------------------------------------------------- planted mistakes fail a pin
 def _pins_pass(golden_dir):
     fx = _load_penalty_fixture(golden_dir)
@@ -496,7 +551,9 @@ def _pins_pass(golden_dir):
               lambda: test_p6_bruteforce(1),
               lambda: test_p7_partition_merge_identity(0),
               lambda: test_p11_q0_closed_form_two_bindings(),
-              lambda: test_p8_three_term_parts_merge_to_attention("defaults")]
+              lambda: test_p8_three_term_parts_merge_to_attention("defaults"),
+              lambda: test_p12_fp8_e4m3_hand_worked(golden_dir),
+              lambda: test_p12_fp8_e4m3_against_code_table()]
     for c in checks:
         try:
             c()
@@ -566,13 +623,32 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
         l[ok] = np.log(np.exp(zc[ok]).sum(axis=1))
         return [parts[0], parts[1], (parts[2][0], l)]
 
+    def fp8_truncating(x):
+        # rounding toward zero instead of to nearest even
+        x = np.asarray(x, np.float64)
+        a = np.abs(x)
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+        ulp = 2.0 ** (np.maximum(e, -6.0) - 3.0)
+        return np.sign(x) * np.floor(a / ulp) * ulp
+
+    def fp8_half_away(x):
+        # ties away from zero instead of to even
+        x = np.asarray(x, np.float64)
+        a = np.abs(x)
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+        ulp = 2.0 ** (np.maximum(e, -6.0) - 3.0)
+        return np.sign(x) * np.floor(a / ulp + 0.5) * ulp
+
     mutants = [("penalty", no_square), ("penalty", no_window), ("bias_block", wrong_sign),
                ("bias_block", swap_qk_roles), ("bias_block", log2_gain), ("attention_head", transposed_kv),
                ("bias_block", first_binding_only), ("bias_block", one_mask_plane),
-               ("three_term_parts", correction_keeps_cap)]
+               ("three_term_parts", correction_keeps_cap), ("fp8_e4m3_round", fp8_truncating),
+               ("fp8_e4m3_round", fp8_half_away)]
     for name, fn in mutants:
         with monkeypatch.context() as m:
             m.setattr(tor, name, fn)
-            if name in ("attention_head", "three_term_parts"):
+            if name in ("attention_head", "three_term_parts", "fp8_e4m3_round"):
                 m.setattr(oracle, name, fn)
             assert not _pins_pass(golden_dir), f"planted mistake {fn.__name__} went unnoticed"
