@@ -1,7 +1,7 @@
 """Throughput of TARA attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5|7]
-                    [--mode fused|partitioned|three-term]
+                    [--mode fused|partitioned|three-term] [--qk8]
 
 A step is one tara_attn_fwd call (metadata encoding, V layout pass, the fused
 attention kernel; in partitioned mode the range passes plus the merge; in
@@ -9,7 +9,9 @@ three-term mode the three Flash Partitions passes plus the merge) over the
 whole workload, inputs already resident in HBM. The default workload is the 107,126-token
 packed sequence (52,751 target + 52,751 guide + 2 x 556 picture + 512 text
 tokens, 107 latent frames) at 56 heads of dim 128 in bf16 with the default
-TARA controls. Prints one JSON line.
+TARA controls. Prints one JSON line. --qk8 takes Q.K in FP8 E4M3 (per-row
+and per-key-tile power-of-two scales; P.V stays bf16); its roofline peak is
+that of the FLOP mix, half at the FP8 MFMA peak and half at the bf16 one.
 
 Effective work per step is 4 * B * H * N^2 * D FLOP (both products over every
 query/key pair; bias skipping removes no contraction work).
@@ -29,6 +31,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
+# Q.K at the FP8 rate and P.V at the bf16 rate, equal FLOP each
+PEAK_QK8_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_FP32_VALU_TFLOPS = 157.3
 METRIC = "TARA attention TFLOP/s and % of bf16 MFMA peak at 107,126 tok × 56 heads"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_headline_traffic.json")
@@ -101,6 +106,7 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--mode", default="fused", choices=["fused", "partitioned", "three-term"])
     ap.add_argument("--partitions", type=int, default=3)
+    ap.add_argument("--qk8", action="store_true", help="8-bit Q.K (bf16 workloads, fused mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
@@ -139,7 +145,7 @@ def main():
     params = tara.make_params(window=cp.window, falloff=cp.falloff, strength=cp.strength, cap=cp.cap,
                               binding=cp.binding, gains=tuple(cp.gains), mode=args.mode,
                               partitions=args.partitions if args.mode == "partitioned" else 1,
-                              chained=tuple(tuple(c) for c in cp.chained))
+                              chained=tuple(tuple(c) for c in cp.chained), qk8=args.qk8)
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     ws = torch.empty(max(tara.tara_workspace_bytes(tara.TARA_BF16 if cfg.dtype == "bf16" else tara.TARA_FP32,
@@ -180,7 +186,8 @@ def main():
     value = flop / (ms_step / 1e3) / 1e12
     k_avg = sum(kms) / len(kms) if kms else float("nan")
     achieved = flop / (k_avg / 1e3) / 1e12
-    traffic = measured_traffic(flop)
+    traffic = None if args.qk8 else measured_traffic(flop)
+    peak = PEAK_QK8_TFLOPS if args.qk8 else PEAK_BF16_TFLOPS
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -192,19 +199,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "fp8 (Q.K) + bf16 (P.V)" if args.qk8 else cfg.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, packed H3-shaped metadata)",
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "config": {"workload": f"{cfg.name} ({args.mode})", "tokens": N, "heads": H, "head_dim": D, "batch": B,
+        "config": {"workload": f"{cfg.name} ({args.mode}{', 8-bit Q.K' if args.qk8 else ''})", "tokens": N, "heads": H, "head_dim": D, "batch": B,
                    "target_tokens": int((lay.seg == 0).sum()), "guide_tokens": int((lay.seg == 1).sum()),
-                   "mode": args.mode, "partitions": info.get("num_partitions"),
+                   "mode": args.mode, "partitions": info.get("num_partitions"), "qk8": args.qk8,
                    "controls": {"window": cfg.params.window, "falloff": cfg.params.falloff,
                                 "strength": cfg.params.strength, "cap": cfg.params.cap,
                                 "binding": cfg.params.binding, "gains": list(cfg.params.gains),
                                 "chained_gains": [list(c) for c in cfg.params.chained]},
                    "block_q": info.get("block_q"), "block_k": info.get("block_k"), "grid": info.get("grid")},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
                      "kernel_ms_avg": round(k_avg, 4), "launches_timed": len(kms),
                      "flop_per_launch": flop},

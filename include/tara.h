@@ -109,7 +109,17 @@ typedef enum {
  *  mode, num_partitions, partition_bounds: see tara_mode_t. partition_bounds
  *    is a host array of num_partitions + 1 non-decreasing key offsets from 0 to
  *    N (empty ranges allowed), or NULL for num_partitions near-equal ranges;
- *    1 <= num_partitions <= TARA_MAX_PARTITIONS. */
+ *    1 <= num_partitions <= TARA_MAX_PARTITIONS.
+ *  qk8: nonzero computes Q . K from 8-bit copies, as the dense 8-bit one-pass
+ *    kernels of the "Three backends" section do (that section names no
+ *    quantisation scheme; this one is): each query row and each tile of 64
+ *    keys is divided by its own power of two, 2^(floor(log2 max|x|) - 7), and
+ *    rounded to FP8 E4M3 (round to nearest even); the FP8 products are summed
+ *    in fp32 and multiplied back by both powers of two. Softmax, bias and P.V
+ *    are unchanged (P and V stay bf16). Requires TARA_BF16 and TARA_MODE_FUSED.
+ *    The result equals exact attention on the rounded Q and K up to fp32
+ *    rounding; against unrounded attention it differs by the E4M3 rounding of
+ *    the logits (relative 2^-4 per element). */
 typedef struct {
   float window;
   float falloff;
@@ -123,6 +133,7 @@ typedef struct {
   int mode;
   int num_partitions;
   const int32_t* partition_bounds;
+  int qk8;
 } tara_params_t;
 
 /* Fills *p with the defaults: window 0.20, falloff 0.25, strength 2.0,

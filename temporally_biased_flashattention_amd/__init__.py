@@ -74,6 +74,7 @@ class TaraParams(ctypes.Structure):
         ("mode", ctypes.c_int),
         ("num_partitions", ctypes.c_int),
         ("partition_bounds", ctypes.POINTER(ctypes.c_int32)),
+        ("qk8", ctypes.c_int),
     ]
 
 
@@ -134,9 +135,10 @@ def make_params(window: float = 0.20, falloff: float = 0.25, strength: float = 2
                 binding: bool = False, gains: Sequence[float] = (), softmax_scale: float = 0.0,
                 mode: str = "fused", partitions: int = 1,
                 bounds: Optional[Sequence[int]] = None,
-                chained: Sequence[Sequence[float]] = ()) -> TaraParams:
+                chained: Sequence[Sequence[float]] = (), qk8: bool = False) -> TaraParams:
     """Builds tara_params_t. gains[i] is the gain of 0-based picture id i
-    under the first binding; chained[j][i] that under binding j + 1."""
+    under the first binding; chained[j][i] that under binding j + 1; qk8
+    selects the 8-bit Q.K product (bf16, fused mode)."""
     p = tara_params_default()
     p.window, p.falloff, p.strength, p.cap = window, falloff, strength, cap
     p.binding_enabled = int(bool(binding))
@@ -159,6 +161,7 @@ def make_params(window: float = 0.20, falloff: float = 0.25, strength: float = 2
         arr = (ctypes.c_int32 * len(bounds))(*[int(x) for x in bounds])
         p._bounds_keepalive = arr  # noqa: SLF001 (keeps the host array alive)
         p.partition_bounds = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    p.qk8 = int(bool(qk8))
     return p
 
 

@@ -34,7 +34,7 @@ bool env_flag(const char* name) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tq, tk, kp, gt, ksum, vt, kmax, opart, lsepart, total;
+  size_t tq, tk, kp, gt, ksum, vt, kmax, k8, ks, opart, lsepart, total;
 };
 
 int npad_of(int N) { return (N + tara::kBlockK - 1) / tara::kBlockK * tara::kBlockK; }
@@ -45,6 +45,12 @@ int num_parts(const tara_params_t* p) {
 
 bool has_partials(const tara_params_t* p) { return p->mode != TARA_MODE_FUSED; }
 
+// 8-bit Q.K: the bf16 path in fused mode only
+bool uses_qk8(tara_dtype_t dtype, const tara_params_t* p) { return p->qk8 && dtype == TARA_BF16; }
+bool qk8_supported(tara_dtype_t dtype, const tara_params_t* p) {
+  return !p->qk8 || (dtype == TARA_BF16 && p->mode == TARA_MODE_FUSED);
+}
+
 int num_bindings(const tara_params_t* p) { return p->num_bindings < 1 ? 1 : p->num_bindings; }
 
 // Pictures of the gain table (0 without binding).
@@ -52,7 +58,8 @@ int table_pictures(const tara_params_t* p) { return p->binding_enabled ? p->num_
 
 // Workspace regions, each 256-byte aligned: per-token encodings (with
 // binding, the per-query gain table), key-tile summaries, V^T (bf16 path),
-// and per-partition O/LSE (partitioned mode).
+// the FP8 copy of K and its tile scales (8-bit Q.K), and per-partition O/LSE
+// (every mode but fused).
 WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
   WsLayout L{};
   const size_t npad = (size_t)npad_of(N), nkt = npad / tara::kBlockK;
@@ -69,6 +76,10 @@ WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tar
   L.ksum = take((size_t)B * nkt * sizeof(tara::KeyTileSummary));
   L.vt = dtype == TARA_BF16 ? take((size_t)B * H * D * npad * 2) : 0;
   L.kmax = dtype == TARA_BF16 ? take((size_t)B * H * nkt * 4) : 0;
+  if (uses_qk8(dtype, p)) {
+    L.k8 = take((size_t)B * H * npad * D);
+    L.ks = take((size_t)B * H * nkt * 4);
+  }
   if (has_partials(p)) {
     const size_t parts = (size_t)num_parts(p);
     L.opart = take(parts * B * H * N * D * 4);
@@ -198,6 +209,7 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D, cons
   if (B < 0 || H < 0 || N < 0) return (size_t)-1;
   if (p->mode == TARA_MODE_PARTITIONED && (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS))
     return (size_t)-1;
+  if (!qk8_supported(dtype, p)) return (size_t)-1;
   if (B == 0 || H == 0 || N == 0) return 0;
   return ws_layout_for(dtype, B, H, N, D, p).total;
 }
@@ -268,6 +280,7 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (p && p->mode == TARA_MODE_THREE_TERM && npad_of(N) / tara::kBlockK > tara::kMaxListTiles)
     return fail(TARA_ERR_BAD_SHAPE, "three-term mode supports N <= 2^20 (its key-tile lists live in LDS)");
   if (int st = check_params(p, N)) return st;
+  if (!qk8_supported(dtype, p)) return fail(TARA_ERR_BAD_PARAM, "qk8 requires TARA_BF16 and TARA_MODE_FUSED");
   if (B == 0 || H == 0 || N == 0) {
     g_info = tara_run_info_t{p->mode, (int)dtype, 0, 0, num_parts(p), 0, tara::kBlockK, 0, 0};
     g_info_valid = true;
@@ -361,6 +374,9 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   aa.npics = ma.num_pictures;
   aa.ksum = ma.ksum;
   aa.kmax = dtype == TARA_BF16 ? reinterpret_cast<const float*>(ws + L.kmax) : nullptr;
+  const bool qk8 = uses_qk8(dtype, p);
+  aa.k8 = qk8 ? reinterpret_cast<const uint8_t*>(ws + L.k8) : nullptr;
+  aa.ks = qk8 ? reinterpret_cast<const float*>(ws + L.ks) : nullptr;
   aa.c = (float)(scale * log2e);
   const double sigma = bias_active ? std::sqrt((double)p->strength * log2e) / (double)p->falloff : 0.0;
   aa.sigma = (float)sigma;
@@ -391,8 +407,14 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                                 const_cast<__bf16*>(aa.vt), B, H, N, npad, D, stream);
     ++launches;
     if (e == hipSuccess) {
-      e = tara::launch_knorm(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
-                             const_cast<float*>(aa.kmax), B, H, N, nkt, D, stream);
+      // key norms per tile; with 8-bit Q.K the same kernel also writes the FP8 keys and tile scales
+      if (qk8)
+        e = tara::launch_kquant(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
+                                const_cast<uint8_t*>(aa.k8), const_cast<float*>(aa.ks), const_cast<float*>(aa.kmax),
+                                B, H, N, npad, nkt, D, stream);
+      else
+        e = tara::launch_knorm(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
+                               const_cast<float*>(aa.kmax), B, H, N, nkt, D, stream);
       ++launches;
     }
   }
@@ -416,7 +438,7 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
       block_q = tara::attn_bf16_block_q(D);
       aa.nqb = (N + block_q - 1) / block_q;
       grid += tara::attn_bf16_grid(aa) * (pass == tara::PASS_RANGE ? parts : 1);
-      e = tara::launch_attn_bf16(aa, D, pass, stream);
+      e = tara::launch_attn_bf16(aa, D, pass, qk8, stream);
     } else {
       block_q = tara::attn_f32_block_q(D);
       aa.nqb = (N + block_q - 1) / block_q;

@@ -91,6 +91,8 @@ struct AttnArgs {
   int npics;               // row length of gt
   const KeyTileSummary* ksum;
   const float* kmax;       // bf16 path: [B*H][nkt] max |k| per key tile
+  const uint8_t* k8;       // 8-bit Q.K: FP8 E4M3 keys [B*H][npad][D]
+  const float* ks;         // 8-bit Q.K: power-of-two scale per key tile [B*H][nkt]
   float c;                 // softmax_scale * log2 e
   float sigma;             // sqrt(strength * log2 e) / falloff  (1/s)
   float w;                 // window * sigma
@@ -116,10 +118,12 @@ hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn
                              int B, int H, int N, int npad, int D, hipStream_t s);
 hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, float* kmax, int B, int H, int N,
                         int nkt, int D, hipStream_t s);
+hipError_t launch_kquant(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, uint8_t* k8, float* ks, float* kmax,
+                         int B, int H, int N, int npad, int nkt, int D, hipStream_t s);
 // Block of query rows per workgroup of the bf16 attention kernel.
 int attn_bf16_block_q(int D);
 int attn_bf16_grid(const AttnArgs& a);
-hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, bool qk8, hipStream_t s);
 int attn_f32_block_q(int D);
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int pass, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16_out, hipStream_t s);

@@ -240,6 +240,93 @@ hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, flo
   return hipGetLastError();
 }
 
+// ------------------------------------------------- 8-bit Q.K: K quantisation
+// FP8 E4M3 (OCP; round to nearest even, as v_cvt_pk_fp8_f32 does) with a
+// power-of-two scale per 64-key tile of a head, 2^(floor(log2 max|k|) - 7),
+// so the tile's largest magnitude lands in [128, 256). Writes
+//   k8[b*H + h][n][d]  the scaled, rounded keys (rows past N are 0),
+//   ks[b*H + h][t]     the tile's scale,
+//   kmax[b*H + h][t]   max |k| over the tile's rows (bf16 values).
+// 256 threads per tile: four adjacent threads per row, D/4 elements each.
+
+// floor(log2 |x|) of a finite x != 0 (exact, subnormals included)
+__device__ __forceinline__ int floor_log2(float x) {
+  int e;
+  (void)frexpf(x, &e);
+  return e - 1;
+}
+
+// Packs four floats (already scaled to |x| < 256) into four E4M3 bytes.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+__global__ __launch_bounds__(256) void kquant_kernel(const __bf16* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
+                                                     int H, int N, int D, int npad, int nkt, uint8_t* __restrict__ k8,
+                                                     float* __restrict__ ks, float* __restrict__ kmax) {
+  __shared__ float wred[2][4];
+  const int t = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int r = threadIdx.x >> 2, qd = threadIdx.x & 3;
+  const int n = t * kBlockK + r;
+  const bool valid = n < N;
+  const int dq = D / 4;
+  const __bf16* kp = k + b * sb + h * sh + (int64_t)(valid ? n : 0) * sn + qd * dq;
+  float v[32];
+  float ss = 0.0f, am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    if (i < dq) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(kp + i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = valid ? (float)x[e] : 0.0f;
+        v[i + e] = f;
+        ss = fmaf(f, f, ss);
+        am = fmaxf(am, fabsf(f));
+      }
+    }
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  float nm = sqrtf(ss);
+  for (int off = 32; off >= 1; off >>= 1) {
+    nm = fmaxf(nm, __shfl_xor(nm, off));
+    am = fmaxf(am, __shfl_xor(am, off));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wred[0][threadIdx.x >> 6] = nm;
+    wred[1][threadIdx.x >> 6] = am;
+  }
+  __syncthreads();
+  nm = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  am = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
+  const int e = am > 0.0f ? floor_log2(am) - 7 : 0;   // scale 2^e
+  uint8_t* dst = k8 + ((int64_t)bh * npad + n) * D + qd * dq;
+#pragma unroll
+  for (int i = 0; i < 32; i += 16) {
+    if (i < dq) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = pack_fp8x4(ldexpf(v[i + 4 * j], -e), ldexpf(v[i + 4 * j + 1], -e), ldexpf(v[i + 4 * j + 2], -e),
+                          ldexpf(v[i + 4 * j + 3], -e));
+      *reinterpret_cast<u32x4*>(dst + i) = w;
+    }
+  }
+  if (threadIdx.x == 0) {
+    ks[(int64_t)bh * nkt + t] = ldexpf(1.0f, e);
+    kmax[(int64_t)bh * nkt + t] = nm;
+  }
+}
+
+hipError_t launch_kquant(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, uint8_t* k8, float* ks, float* kmax,
+                         int B, int H, int N, int npad, int nkt, int D, hipStream_t s) {
+  dim3 grid(nkt, B * H);
+  hipLaunchKernelGGL(kquant_kernel, grid, dim3(256), 0, s, k, sb, sh, sn, H, N, D, npad, nkt, k8, ks, kmax);
+  return hipGetLastError();
+}
+
 // --------------------------------------------------------- bf16 MFMA kernel
 // One workgroup = NW waves x 32 query rows of one (batch, head). Per 64-key
 // tile t every wave runs a two-phase software pipeline so that its MFMAs and
@@ -282,7 +369,7 @@ __device__ __forceinline__ void dma16(BufRange r, uint32_t voff, uint32_t soff, 
 // writes 64 lanes x 16 bytes contiguously at a uniform LDS address. A padded
 // tile of BLK whole 1-KB blocks (rows of ROWB bytes holding DATA 16-byte data
 // chunks) is staged by all NW waves: wave w takes blocks w, w + NW, ...
-// (PER_MAX DMAs for waves w < BLK % NW, PER_MIN for the others). A lane whose
+// (PER_MAX DMAs for waves w < BLK % NW, PER_MIN, possibly 0, for the others). A lane whose
 // 16 bytes fall on a row's pad chunk re-reads chunk 0 of its row (never read
 // back). Buffer loads rather than global_load_lds: the latter is FLAT-encoded,
 // and while one is in flight the compiler cannot count LDS reads, so every
@@ -292,7 +379,7 @@ struct TileDma {
   static constexpr int PER_MIN = BLK / NW;
   static constexpr int PER_MAX = (BLK + NW - 1) / NW;
   static constexpr int NEXTRA = BLK % NW;
-  static_assert(PER_MIN >= 1, "every wave stages at least one block");
+  static_assert(PER_MAX >= 1, "a tile is at least one block");
   uint32_t voff[PER_MAX];   // byte offset of this lane's 16 bytes in its tile
   int row[PER_MAX];         // tile row of those bytes
   __device__ void init(int wave, int lane, uint32_t row_bytes) {
@@ -352,6 +439,29 @@ __device__ __forceinline__ bf16x8 kfrag(const __bf16* kr0, int i) {
 template <int VROW, int NDB>
 __device__ __forceinline__ bf16x8 vfrag(const __bf16* vr0, int i) {
   return *reinterpret_cast<const bf16x8*>(vr0 + (i % NDB) * 32 * VROW + (i / NDB) * 16);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 8-bit Q.K: S^T (32 keys x 32 queries) += K8 (32 keys x 64 dims, FP8 E4M3)
+// x Q8^T with fp32 accumulation (v_mfma_scale_f32_32x32x64_f8f6f4, block
+// scales 1.0). Operand layout: lane l holds row (A) / column (B) l % 32 and the
+// 32 consecutive dims 32*(l/32) .. +31 of the 64.
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 k8, i32x8 q8, f32x16 acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k8, q8, acc, 0, 0, 0, 127, 0, 127);
+}
+
+// i-th fp8 K fragment of phase A: key block i & 1, 64-dim step i >> 1 (32
+// bytes from the lane's K row, LDS row pitch KROWB bytes).
+template <int KROWB>
+__device__ __forceinline__ i32x8 kfrag8(const char* kr0, int i) {
+  const char* p = kr0 + (i & 1) * 32 * KROWB + (i >> 1) * 64;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+  i32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
 }
 
 // max of three floats as one v_max3_f32. The operands here are scores (finite,
@@ -445,7 +555,9 @@ __device__ __forceinline__ bool tile_class_lane(const KeyTileSummary& sm, bool p
 }
 
 // Per-element logits of a key tile, in place (log2 units), keys outside
-// [k0, k1) -> -inf. Fused / range passes: x = s*c - penalty + binding, where
+// [k0, k1) -> -inf; cmul turns a raw product into log2 units (the softmax
+// scale times log2 e, times the fp8 scales for 8-bit Q.K). Fused / range
+// passes: x = s*cmul - penalty + binding, where
 // binding is the query's summed log2 gain of the key's picture (gtq: this row
 // of the gain table, in LDS; read only when the tile holds bound picture
 // keys). Term passes keep only their keys (see PASS_TERM_*). A key is a biased
@@ -454,7 +566,7 @@ __device__ __forceinline__ bool tile_class_lane(const KeyTileSummary& sm, bool p
 template <int PASS>
 __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, float tq, bool has_pic,
                                           const float* gtq, bool partial, int k0, int k1, const float* tkb,
-                                          const int* kpb, const AttnArgs& a) {
+                                          const int* kpb, const AttnArgs& a, float cmul) {
   const bool qb = tq == tq;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -471,11 +583,11 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
         const float sv = s[kb][c2 * 8 + e];
         const bool isg = tk == tk;
         float x;
-        if (PASS == PASS_TERM_A) x = isg ? -INFINITY : sv * a.c;
-        else if (PASS == PASS_TERM_B) x = isg ? fmaf(sv, a.c, qb ? -a.cap2 : 0.0f) : -INFINITY;
+        if (PASS == PASS_TERM_A) x = isg ? -INFINITY : sv * cmul;
+        else if (PASS == PASS_TERM_B) x = isg ? fmaf(sv, cmul, qb ? -a.cap2 : 0.0f) : -INFINITY;
         else if (PASS == PASS_TERM_C)
-          x = isg && qb ? fmaf(sv, a.c, __log2f(1.0f - fast_exp2(pen - a.cap2)) - pen) : -INFINITY;
-        else x = fmaf(sv, a.c, -pen);
+          x = isg && qb ? fmaf(sv, cmul, __log2f(1.0f - fast_exp2(pen - a.cap2)) - pen) : -INFINITY;
+        else x = fmaf(sv, cmul, -pen);
         s[kb][c2 * 8 + e] = x;
       }
     }
@@ -504,21 +616,24 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
   }
 }
 
-template <int D, int NW, int PASS>
+template <int D, int NW, int PASS, bool Q8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr bool PART = PASS != PASS_FUSED;   // writes one partition's (O_p, LSE_p)
   constexpr bool TERM = PASS >= PASS_TERM_A;  // visits a listed subset of the key tiles
+  static_assert(!Q8 || PASS == PASS_FUSED, "8-bit Q.K is built for the fused pass");
   constexpr int BQ = NW * 32;              // query rows per workgroup
-  constexpr int KROW = D + 8;              // padded LDS pitch of a K row (elements)
+  constexpr int KROW = D + 8;              // padded LDS pitch of a bf16 K row (elements)
+  // LDS pitch of a K row in bytes (FP8 rows: D bytes + a 16-byte pad)
+  constexpr int KROWB = Q8 ? D + 16 : KROW * 2;
   constexpr int VROW = kBlockK + 8;        // padded LDS pitch of a V^T row (elements)
-  constexpr int KTILE = kBlockK * KROW;
+  constexpr int KTILE = kBlockK * KROWB / 2;   // K tile size in bf16 elements
   constexpr int VTILE = D * VROW;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int NA = 2 * NKK;              // MFMAs (and LDS fragments) of phase A
+  constexpr int NA = Q8 ? 2 * (D / 64) : 2 * NKK;   // MFMAs of phase A (K fragments)
   constexpr int NB = 4 * NDB;              // MFMAs (and LDS fragments) of phase B
-  static_assert(NA % 4 == 0 && NB % 4 == 0, "ring positions carry over between the phases");
+  static_assert((Q8 || NA % 4 == 0) && NB % 4 == 0, "ring positions carry over between the phases");
   // LDS ring of NS stages: K tiles in slots 0..NS-1, then V^T tiles in slots 0..NS-1
   constexpr int NS = kStages;
   static_assert(NS == 3, "slot arithmetic and the DMA wait count assume three stages");
@@ -549,11 +664,47 @@ void attn_bf16_kernel(AttnArgs a) {
   const int qrow = qblk * BQ + wave * 32 + lq;
   const bool qvalid = qrow < N;
   const int qr = qvalid ? qrow : N - 1;
-  bf16x8 qf[NKK];
+  bf16x8 qf[Q8 ? 1 : NKK];
+  i32x8 qf8[Q8 ? D / 64 : 1];
+  float q_ss = 0.0f;                       // |q|^2 of the lane's share of the row
+  float cq = a.c;                          // 8-bit Q.K: softmax scale * log2 e * the row's scale
   {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)qr * a.q_sn;
+    if constexpr (!Q8) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
+      for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q_ss = fmaf((float)qf[kk][e], (float)qf[kk][e], q_ss);
+    } else {
+      // FP8 E4M3 with the row's power-of-two scale 2^(floor(log2 max|q|) - 7);
+      // this lane holds dims 64*st + 32*hh .. +31 of each 64-dim step st
+      float qv[D / 2];
+      float am = 0.0f;
+#pragma unroll
+      for (int st = 0; st < D / 64; ++st)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 x8 = *reinterpret_cast<const bf16x8*>(qp + st * 64 + hh * 32 + u * 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = (float)x8[e];
+            qv[st * 32 + u * 8 + e] = f;
+            q_ss = fmaf(f, f, q_ss);
+            am = fmaxf(am, fabsf(f));
+          }
+        }
+      am = xor32_max(am);
+      const int e = am > 0.0f ? floor_log2(am) - 7 : 0;
+      cq = a.c * ldexpf(1.0f, e);
+#pragma unroll
+      for (int st = 0; st < D / 64; ++st)
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          qf8[st][w] = (int)pack_fp8x4(ldexpf(qv[st * 32 + w * 4], -e), ldexpf(qv[st * 32 + w * 4 + 1], -e),
+                                       ldexpf(qv[st * 32 + w * 4 + 2], -e), ldexpf(qv[st * 32 + w * 4 + 3], -e));
+    }
   }
   const float tq = a.tq[(int64_t)b * N + qr];
   const bool qbiased = tq == tq;
@@ -647,13 +798,15 @@ void attn_bf16_kernel(AttnArgs a) {
 
   // staging: buffer ranges over this head's K rows and V^T rows; per-lane
   // 32-bit offsets within a tile, per-tile scalar offsets
-  const __bf16* kg = static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh;
+  // (8-bit Q.K stages the FP8 copy of K, rows of D bytes, zero past N)
+  const void* kg = Q8 ? static_cast<const void*>(a.k8 + (int64_t)bh * a.npad * D)
+                      : static_cast<const void*>(static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh);
   const __bf16* vg = a.vt + (int64_t)bh * D * a.npad;
-  const uint32_t k_sn_bytes = (uint32_t)(a.k_sn * 2);
-  const BufRange rk{kg, (uint32_t)(N - 1) * k_sn_bytes + D * 2};
+  const uint32_t k_sn_bytes = Q8 ? (uint32_t)D : (uint32_t)(a.k_sn * 2);
+  const BufRange rk{kg, Q8 ? (uint32_t)(a.npad * D) : (uint32_t)(N - 1) * k_sn_bytes + D * 2};
   const BufRange rv{vg, (uint32_t)(D * a.npad * 2)};
   static_assert(KTILE * 2 % 1024 == 0 && VTILE * 2 % 1024 == 0, "tiles are whole 1-KB blocks");
-  using KDma = TileDma<KROW * 2, D / 8, KTILE * 2 / 1024, NW>;
+  using KDma = TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW>;
   using VDma = TileDma<VROW * 2, kBlockK / 8, VTILE * 2 / 1024, NW>;
   KDma kdma;
   VDma vdma;
@@ -664,7 +817,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const int rows_left = N - kk * kBlockK;
     const uint32_t soff = (uint32_t)kk * kBlockK * k_sn_bytes;
     char* l = reinterpret_cast<char*>(KBUF(sk));
-    if (rows_left >= kBlockK) kdma.template issue<false>(rk, soff, rows_left, k_sn_bytes, l, wave);
+    if (Q8 || rows_left >= kBlockK) kdma.template issue<false>(rk, soff, rows_left, k_sn_bytes, l, wave);
     else kdma.template issue<true>(rk, soff, rows_left, k_sn_bytes, l, wave);
   };
   auto stage_v = [&](int kv, int sv) {
@@ -684,20 +837,13 @@ void attn_bf16_kernel(AttnArgs a) {
   const KsumConstPtr ks_c = (KsumConstPtr)(a.ksum + (int64_t)b * a.nkt);
   const __attribute__((address_space(4))) float* kmax_c =
       (const __attribute__((address_space(4))) float*)(a.kmax + (int64_t)bh * a.nkt);
+  // 8-bit Q.K: the key tiles' power-of-two scales
+  const __attribute__((address_space(4))) float* kscale_c =
+      (const __attribute__((address_space(4))) float*)(Q8 ? a.ks + (int64_t)bh * a.nkt : a.kmax);
   const int krow_lane = perm32(lq);
-  // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum
-  float qn_c;
-  {
-    float ss = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = (float)qf[kk][e];
-        ss = fmaf(v, v, ss);
-      }
-    qn_c = sqrtf(xor32_sum(ss)) * a.c * (1.0f + 0x1.0p-10f);
-  }
+  // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum;
+  // with 8-bit Q.K also by (1 + 2^-4)^2 for the rounding of q and k to E4M3
+  const float qn_c = sqrtf(xor32_sum(q_ss)) * a.c * (Q8 ? 1.13f : 1.0f + 0x1.0p-10f);
 
   f32x16 o[NDB];
 #pragma unroll
@@ -705,12 +851,17 @@ void attn_bf16_kernel(AttnArgs a) {
   float m_used, lsum = 0.0f;
   f32x16 x[2];   // X_t = S_t * c + bias - m_used (exp2 argument)
   KeyTileSummary sm_next;
-  float kmax_next;
+  float kmax_next, kscale_next = 1.0f;
   // LDS fragment ring: fragment j of the per-wave stream (K_{t+1} fragments of
-  // phase A, then V_t fragments of phase B, then K_{t+2} ...) sits in fr[j & 3]
+  // phase A, then V_t fragments of phase B, then K_{t+2} ...) sits in fr[j & 3];
+  // with 8-bit Q.K the K fragments (32 bytes each) go through kf8 instead
   bf16x8 fr[4];
+  i32x8 kf8[2];
   const int koff_lane = krow_lane * KROW + hh * 8;   // phase A reads K rows kb*32 + perm32(lq)
+  const int koffb8 = krow_lane * KROWB + hh * 32;    // the same rows, FP8 bytes
   const int voff_lane = lq * VROW + hh * 8;          // phase B reads V^T rows db*32 + lq
+  // raw Q.K products to log2 units for a tile (cq: the row part; times the tile's scale)
+  auto tile_mul = [&](float kscale) { return Q8 ? cq * kscale : a.c; };
 
   {
     // prologue: the first three tiles' K into K slots 0..2, the first two
@@ -724,16 +875,23 @@ void attn_bf16_kernel(AttnArgs a) {
     stage_v(tile_at(1), 1);
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
+    if constexpr (Q8) {
+      const char* k8r = reinterpret_cast<const char*>(KBUF(0)) + koffb8;
+      x[0] = x[1] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NA; ++i) x[i & 1] = mfma_fp8(kfrag8<KROWB>(k8r, i), qf8[i >> 1], x[i & 1]);
+    } else {
+      qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
+    }
     const int kbase = tile0 * kBlockK;
     const bool partial = kbase < k0 || kbase + kBlockK > k1;
     const KeyTileSummary sm0 = load_summary(ks_c, tile0);
     const float gpic0 = gtq[max(sm0.pic, 0)];
     float brow;
     const bool lane_elem = tile_class_lane<PASS>(sm0, partial, qbiased, tq, gpic0, a, &brow);
-    float cc = a.c;
+    float cc = tile_mul(Q8 ? kscale_c[tile0] : 1.0f);
     if (wave_any(lane_elem)) {
-      elem_bias<PASS>(x, kbase, hh, tq, (sm0.kind & KT_HAS_PICTURE) != 0, gtq, partial, k0, k1, tkb, kpb, a);
+      elem_bias<PASS>(x, kbase, hh, tq, (sm0.kind & KT_HAS_PICTURE) != 0, gtq, partial, k0, k1, tkb, kpb, a, cc);
       brow = 0.0f;
       cc = 1.0f;
     }
@@ -751,13 +909,19 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(x[kb][r], cc, off);
     sm_next = load_summary(ks_c, tile_at(1));
     kmax_next = kmax_c[tile_at(1)];
-    const __bf16* kr0 = KBUF(1) + koff_lane;
-    fr[0] = kfrag<KROW>(kr0, 0);
-    fr[1] = kfrag<KROW>(kr0, 1);
-    fr[2] = kfrag<KROW>(kr0, 2);
+    if (Q8) kscale_next = kscale_c[tile_at(1)];
+    if constexpr (Q8) {
+      kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(1)) + koffb8, 0);
+    } else {
+      const __bf16* kr0 = KBUF(1) + koff_lane;
+      fr[0] = kfrag<KROW>(kr0, 0);
+      fr[1] = kfrag<KROW>(kr0, 1);
+      fr[2] = kfrag<KROW>(kr0, 2);
+    }
     // every wave is done with K slot 0 before iteration t0 restages it
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next));
+    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next),
+                 "s"(kscale_next));
   }
 
   // ring slots at step t (visiting tile T_t): K and V^T of T_t in s0, of
@@ -776,6 +940,7 @@ void attn_bf16_kernel(AttnArgs a) {
     if (TERM) tv4 = tlist[min(t + 4, ntiles - 1)];
     const KeyTileSummary sm1 = sm_next;
     const float kmax1 = kmax_next;
+    const float kscale1 = kscale_next;
     // a one-picture tile's bias is this row's gain-table entry for the
     // picture (read every tile, so no path waits on a pending load)
     const float gpic1 = gtq[max(sm1.pic, 0)];
@@ -800,30 +965,51 @@ void attn_bf16_kernel(AttnArgs a) {
       x[kb][r + 1] = p1;
       pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
     };
+    if constexpr (Q8) {
+      // four (D 128) or two (D 64) FP8 products, the K fragments one ahead;
+      // the V_t fragments for phase B are fetched under the last one
+      const char* k8r = reinterpret_cast<const char*>(KBUF(s1)) + koffb8;
+      constexpr int EPM = 16 / NA;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int j = i + 3;
-      if (j < NA) fr[j & 3] = kfrag<KROW>(kr0, j);
-      else fr[j & 3] = vfrag<VROW, NDB>(vr0, j - NA);
-      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
-      if (i < 16) exp_pair(i);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < NA; ++i) {
+        if (i + 1 < NA) {
+          kf8[(i + 1) & 1] = kfrag8<KROWB>(k8r, i + 1);
+        } else {
+          fr[0] = vfrag<VROW, NDB>(vr0, 0);
+          fr[1] = vfrag<VROW, NDB>(vr0, 1);
+          fr[2] = vfrag<VROW, NDB>(vr0, 2);
+        }
+        sn[i & 1] = mfma_fp8(kf8[i & 1], qf8[i >> 1], sn[i & 1]);
+#pragma unroll
+        for (int u = 0; u < EPM; ++u) exp_pair(i * EPM + u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int j = i + 3;
+        if (j < NA) fr[j & 3] = kfrag<KROW>(kr0, j);
+        else fr[j & 3] = vfrag<VROW, NDB>(vr0, j - NA);
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
+        if (i < 16) exp_pair(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = NA; i < 16; ++i) exp_pair(i);
     }
-#pragma unroll
-    for (int i = NA; i < 16; ++i) exp_pair(i);
     // keep P_t in this block (the PV product that reads it follows the
     // bias-class branch)
     asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]));
 
     // bias class of tile t+1 (rare per-element path before phase B)
     float brow = 0.0f;
-    float cc = a.c;
+    float cc = tile_mul(kscale1);
     bool need_max = false;
     if (has1) {
       const bool lane_elem = tile_class_lane<PASS>(sm1, partial1, qbiased, tq, gpic1, a, &brow);
       if (wave_any(lane_elem)) {
         elem_bias<PASS>(sn, kbase1, hh, tq, (sm1.kind & KT_HAS_PICTURE) != 0, gtq, partial1, k0, k1, tkb, kpb,
-                        a);
+                        a, cc);
         brow = 0.0f;
         cc = 1.0f;
         need_max = true;
@@ -853,8 +1039,10 @@ void attn_bf16_kernel(AttnArgs a) {
     wait_staged();
     sm_next = load_summary(ks_c, tw2);
     kmax_next = kmax_c[tw2];
+    if (Q8) kscale_next = kscale_c[tw2];
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next));
+    asm volatile("" ::"s"(sm_next.kind), "s"(sm_next.lo), "s"(sm_next.hi), "s"(sm_next.pic), "s"(kmax_next),
+                 "s"(kscale_next));
     stage_v(tw2, s2);
 
     // phase B: O^T += V_t^T P_t^T | row sum of P_t, X_{t+1} = S_{t+1} c +
@@ -865,7 +1053,8 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < NB; ++i) {
       const int j = i + 3;
       if (j < NB) fr[j & 3] = vfrag<VROW, NDB>(vr0, j);
-      else fr[j & 3] = kfrag<KROW>(kn0, j - NB);
+      else if (!Q8) fr[j & 3] = kfrag<KROW>(kn0, j - NB);
+      else if (j == NB) kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(s2)) + koffb8, 0);
       const int db = i % NDB, kc = i / NDB;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
       // spread 32 sums and 32 scale-FMAs over the fragments
@@ -951,21 +1140,26 @@ int attn_bf16_block_q(int) { return kWaves * 32; }
 int attn_bf16_grid(const AttnArgs& a) { return a.nqb * a.B * a.H; }
 
 template <int D>
-void launch_attn_bf16_d(const AttnArgs& a, int pass, dim3 grid, dim3 block, hipStream_t s) {
+void launch_attn_bf16_d(const AttnArgs& a, int pass, bool qk8, dim3 grid, dim3 block, hipStream_t s) {
   switch (pass) {
-    case PASS_FUSED: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED>), grid, block, 0, s, a); break;
-    case PASS_RANGE: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE>), grid, block, 0, s, a); break;
-    case PASS_TERM_A: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_A>), grid, block, 0, s, a); break;
-    case PASS_TERM_B: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_B>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_C>), grid, block, 0, s, a); break;
+    case PASS_FUSED:
+      if (qk8) hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, false>), grid, block, 0, s, a);
+      break;
+    case PASS_RANGE: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE, false>), grid, block, 0, s, a); break;
+    case PASS_TERM_A: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_A, false>), grid, block, 0, s, a); break;
+    case PASS_TERM_B: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_B, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_C, false>), grid, block, 0, s, a); break;
   }
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, hipStream_t s) {
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, bool qk8, hipStream_t s) {
+  // 8-bit Q.K exists for the one-pass form only (the host rejects the rest)
+  if (qk8 && pass != PASS_FUSED) return hipErrorInvalidValue;
   dim3 grid(attn_bf16_grid(a), pass == PASS_RANGE ? a.nparts : 1);
   dim3 block(kWaves * 64);
-  if (D == 128) launch_attn_bf16_d<128>(a, pass, grid, block, s);
-  else launch_attn_bf16_d<64>(a, pass, grid, block, s);
+  if (D == 128) launch_attn_bf16_d<128>(a, pass, qk8, grid, block, s);
+  else launch_attn_bf16_d<64>(a, pass, qk8, grid, block, s);
   return hipGetLastError();
 }
 

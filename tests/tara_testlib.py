@@ -29,11 +29,11 @@ def log(msg: str):
     sys.stdout.flush()
 
 
-def tara_params(p: ti.Params, mode="fused", partitions=1, bounds=None, softmax_scale=0.0):
+def tara_params(p: ti.Params, mode="fused", partitions=1, bounds=None, softmax_scale=0.0, qk8=False):
     return tara.make_params(window=p.window, falloff=p.falloff, strength=p.strength, cap=p.cap,
                             binding=p.binding, gains=tuple(p.gains), softmax_scale=softmax_scale,
                             mode=mode, partitions=partitions, bounds=bounds,
-                            chained=tuple(tuple(c) for c in p.chained))
+                            chained=tuple(tuple(c) for c in p.chained), qk8=qk8)
 
 
 def device_meta(lay: ti.Layout, device="cuda", batch=1):
@@ -50,7 +50,7 @@ def device_meta(lay: ti.Layout, device="cuda", batch=1):
 
 
 def run_gpu(q, k, v, lay: ti.Layout, p: ti.Params, mode="fused", partitions=1, bounds=None,
-            softmax_scale=0.0, layout="bhnd", use_mask=True, heads=None, rows=None):
+            softmax_scale=0.0, layout="bhnd", use_mask=True, heads=None, rows=None, qk8=False):
     """q, k, v: CPU tensors [B, H, N, D]. Returns (O fp32 CPU, LSE fp32 CPU),
     restricted to the given heads and query rows when those are given."""
     dev = "cuda"
@@ -60,7 +60,7 @@ def run_gpu(q, k, v, lay: ti.Layout, p: ti.Params, mode="fused", partitions=1, b
     else:   # stored [B, N, H, D], passed as a [B, H, N, D] view
         qd, kd, vd = (x.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3) for x in (q, k, v))
     seg, tim, pic, mask = device_meta(lay, dev, B)
-    params = tara_params(p, mode, partitions, bounds, softmax_scale)
+    params = tara_params(p, mode, partitions, bounds, softmax_scale, qk8)
     o, lse = tara.attn_fwd(qd, kd, vd, seg, tim, pic, mask if use_mask else None, params)
     torch.cuda.synchronize()
     del qd, kd, vd

@@ -4,6 +4,8 @@ errors are detected before any device work, so these calls never reach HIP)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -39,8 +41,24 @@ def test_params_struct_matches_header_defaults():
     assert p.num_bindings == 1
     assert all(p.picture_gain[j][i] == 1.0 for j in range(4) for i in range(16))
     assert p.softmax_scale == 0.0
-    # ctypes layout: 4 floats, 3 ints, 4x16 floats, float, 2 ints, pointer
-    assert ctypes.sizeof(tara.TaraParams) == 4 * 4 + 3 * 4 + 64 * 4 + 4 + 2 * 4 + 8
+    assert p.qk8 == 0
+    # ctypes layout: 4 floats, 3 ints, 4x16 floats, float, 2 ints, pointer, int (+4 padding)
+    assert ctypes.sizeof(tara.TaraParams) == 4 * 4 + 3 * 4 + 64 * 4 + 4 + 2 * 4 + 8 + 8
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs a C compiler")
+def test_params_layout_matches_c(tmp_path):
+    """The ctypes mirror of tara_params_t has the C compiler's size and offsets."""
+    fields = [n for n, _ in tara.TaraParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"tara.h\"\nint main(void) {\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(tara_params_t, {n}));\n' for n in fields)
+                   + '  printf("%zu\\n", sizeof(tara_params_t));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(tara.TaraParams, n).offset for n in fields] + [ctypes.sizeof(tara.TaraParams)]
+    assert got == want
 
 
 def _al(x):
@@ -65,6 +83,13 @@ def test_workspace_bytes():
     pb = tara.make_params(binding=True, gains=(1.25, 0.75, 0.75), chained=((0.9, 1.1, 1.0),))
     assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, pb) == meta + _al(B * N * 3 * 4)   # gain table
     assert tara.tara_workspace_bytes(tara.TARA_BF16, 0, H, N, D, p) == 0
+    p8 = tara.make_params(qk8=True)   # FP8 keys [B*H][npad][D] and one scale per key tile
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p8) == (
+        meta + bf16_extra + _al(B * H * npad * D) + _al(B * H * nkt * 4))
+    with pytest.raises(tara.TaraError):
+        tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, p8)
+    with pytest.raises(tara.TaraError):
+        tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, tara.make_params(qk8=True, mode="three-term"))
     with pytest.raises(tara.TaraError):
         tara.tara_workspace_bytes(tara.TARA_BF16, 1, 1, 10, 96, p)
     with pytest.raises(tara.TaraError):
@@ -126,6 +151,10 @@ def test_rejections(lib):
     p = P()
     p.mode = 7
     assert call(lib, p) == -6
+    # 8-bit Q.K: bf16 and fused mode only
+    assert call(lib, tara.make_params(qk8=True), dtype=tara.TARA_FP32, strides=(2 * 100 * 128, 100 * 128, 128)) == -6
+    assert call(lib, tara.make_params(qk8=True, mode="partitioned", partitions=2)) == -6
+    assert call(lib, tara.make_params(qk8=True, mode="three-term")) == -6
     # three-term passes keep their key-tile lists in LDS: N <= 2^20
     assert call(lib, tara.make_params(mode="three-term"), N=(1 << 20) + 64, H=1) == -2
 
