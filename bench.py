@@ -1,12 +1,14 @@
 """Throughput of TARA attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5|7]
-                    [--mode fused|partitioned|three-term] [--qk8]
+                    [--mode fused|partitioned|three-term|dense-bias|frame-loop] [--qk8]
 
 A step is one tara_attn_fwd call (metadata encoding, V layout pass, the fused
 attention kernel; in partitioned mode the range passes plus the merge; in
-three-term mode the three Flash Partitions passes plus the merge) over the
-whole workload, inputs already resident in HBM. The default workload is the 107,126-token
+three-term mode the three Flash Partitions passes plus the merge; the
+dense-bias baseline writes the whole bias tensor and then reads it; the
+frame-loop baseline launches the fused pass once per target latent frame and
+once for the other rows) over the whole workload, inputs already resident in HBM. The default workload is the 107,126-token
 packed sequence (52,751 target + 52,751 guide + 2 x 556 picture + 512 text
 tokens, 107 latent frames) at 56 heads of dim 128 in bf16 with the default
 TARA controls. Prints one JSON line. --qk8 takes Q.K in FP8 E4M3 (per-row
@@ -104,7 +106,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline")
-    ap.add_argument("--mode", default="fused", choices=["fused", "partitioned", "three-term"])
+    ap.add_argument("--mode", default="fused",
+                    choices=["fused", "partitioned", "three-term", "dense-bias", "frame-loop"])
     ap.add_argument("--partitions", type=int, default=3)
     ap.add_argument("--qk8", action="store_true", help="8-bit Q.K (bf16 workloads, fused mode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -142,9 +145,11 @@ def main():
     # mask: [1, N], or [J, 1, N] with one plane per chained binding
     mask = None if lay.mask is None else torch.from_numpy(lay.mask)[..., None, :].contiguous().to(dev)
     cp = cfg.params
+    bounds = ti.frame_loop_bounds(lay) if args.mode == "frame-loop" else None
+    nparts = len(bounds) - 1 if bounds else args.partitions if args.mode == "partitioned" else 1
     params = tara.make_params(window=cp.window, falloff=cp.falloff, strength=cp.strength, cap=cp.cap,
                               binding=cp.binding, gains=tuple(cp.gains), mode=args.mode,
-                              partitions=args.partitions if args.mode == "partitioned" else 1,
+                              partitions=nparts, bounds=bounds,
                               chained=tuple(tuple(c) for c in cp.chained), qk8=args.qk8)
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)

@@ -70,8 +70,27 @@ typedef enum { TARA_BF16 = 0, TARA_FP32 = 1 } tara_dtype_t;
  * closer than the saturation gap window + falloff*sqrt(cap/strength). Each
  * pass visits only the key tiles holding keys of its term. N <= 2^20;
  * num_partitions and partition_bounds are ignored.
+ * Two baselines, kept for comparison rather than use:
+ * DENSE_BIAS: the bias of every (query, key) pair is first written to the
+ * workspace as a dense fp32 tensor [B][N][npad] (npad = N rounded up to a
+ * multiple of 64), and one fused pass then reads it instead of evaluating the
+ * rule: the dense bias tensor that the "Three backends" section says the
+ * Flash Partitions evaluation avoids building. TARA_BF16 only; the workspace
+ * grows by 4*B*N*npad bytes (about 46 GB at N = 107,126).
+ * FRAME_LOOP: the fused pass launched once per query range, in order on the
+ * stream, each range against all keys: the per-frame attention loop that the
+ * one-pass kernels of that section drop. The num_partitions ranges are given
+ * by partition_bounds as query-row offsets (for instance one range per latent
+ * frame of the target clip and one for the remaining rows), or are near-equal
+ * when it is NULL; 1 <= num_partitions <= max(N, 1).
  * All modes return the same O and LSE up to rounding. */
-typedef enum { TARA_MODE_FUSED = 0, TARA_MODE_PARTITIONED = 1, TARA_MODE_THREE_TERM = 2 } tara_mode_t;
+typedef enum {
+  TARA_MODE_FUSED = 0,
+  TARA_MODE_PARTITIONED = 1,
+  TARA_MODE_THREE_TERM = 2,
+  TARA_MODE_DENSE_BIAS = 3,
+  TARA_MODE_FRAME_LOOP = 4
+} tara_mode_t;
 
 typedef enum {
   TARA_OK = 0,
@@ -107,9 +126,10 @@ typedef enum {
  *    mask_weight and the gains.
  *  softmax_scale: multiplies Q . K only; 0 selects 1/sqrt(D).
  *  mode, num_partitions, partition_bounds: see tara_mode_t. partition_bounds
- *    is a host array of num_partitions + 1 non-decreasing key offsets from 0 to
- *    N (empty ranges allowed), or NULL for num_partitions near-equal ranges;
- *    1 <= num_partitions <= TARA_MAX_PARTITIONS.
+ *    is a host array of num_partitions + 1 non-decreasing offsets from 0 to N
+ *    (key offsets in PARTITIONED mode, query-row offsets in FRAME_LOOP mode;
+ *    empty ranges allowed), or NULL for num_partitions near-equal ranges;
+ *    PARTITIONED: 1 <= num_partitions <= TARA_MAX_PARTITIONS.
  *  qk8: nonzero computes Q . K from 8-bit copies, as the dense 8-bit one-pass
  *    kernels of the "Three backends" section do (that section names no
  *    quantisation scheme; this one is): each query row and each tile of 64
@@ -145,7 +165,8 @@ void tara_params_default(tara_params_t* p);
  * of 256). It holds per-token encodings of the metadata (with binding, a
  * per-query table of the summed log gains of every picture), per-key-tile
  * summaries, V laid out key-contiguous per (batch, head, dim) for the bf16
- * path, and per-partition O/LSE in the partitioned and three-term modes. Returns 0 for an empty
+ * path, per-partition O/LSE in the partitioned and three-term modes, the FP8
+ * keys with qk8 and the dense bias in DENSE_BIAS mode. Returns 0 for an empty
  * call (B, H or N == 0) and (size_t)-1 for arguments tara_attn_fwd would reject
  * (p == NULL, bad dtype or head dim, bad partition count). */
 size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
@@ -202,7 +223,7 @@ typedef struct {
   int dtype;             /* tara_dtype_t */
   int bias_active;       /* strength > 0 and cap > 0 */
   int binding_active;    /* binding_enabled and some gain != 1 */
-  int num_partitions;    /* 1 in fused mode */
+  int num_partitions;    /* 1 in fused mode; query ranges in FRAME_LOOP mode */
   int block_q;           /* query rows per workgroup of the attention kernel */
   int block_k;           /* keys per tile */
   int grid;              /* workgroups of the attention kernel (all partitions) */

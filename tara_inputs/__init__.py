@@ -155,6 +155,15 @@ def make_layout(frames: int, target_hw: tuple, guide_hw: tuple, pictures: int,
     return Layout(seg, time, pic, frame, m)
 
 
+def frame_loop_bounds(lay: Layout) -> List[int]:
+    """Query-row ranges of a per-frame loop: one range per run of target rows
+    of one latent frame, and one per run of the other rows between them.
+    Returns the offsets [0, ..., N]."""
+    key = np.where(lay.seg == SEG_TARGET, lay.frame.astype(np.int64), -1)
+    cuts = np.nonzero(key[1:] != key[:-1])[0] + 1
+    return [0] + [int(c) for c in cuts] + [lay.n]
+
+
 @dataclasses.dataclass
 class Config:
     cid: int

@@ -23,6 +23,7 @@ from typing import Optional, Sequence
 __all__ = [
     "TARA_SEG_TARGET", "TARA_SEG_GUIDE", "TARA_SEG_PICTURE", "TARA_SEG_OTHER",
     "TARA_BF16", "TARA_FP32", "TARA_MODE_FUSED", "TARA_MODE_PARTITIONED", "TARA_MODE_THREE_TERM",
+    "TARA_MODE_DENSE_BIAS", "TARA_MODE_FRAME_LOOP",
     "TaraError", "TaraLibraryMissing", "TaraParams", "TaraRunInfo",
     "tara_params_default", "make_params", "tara_workspace_bytes", "tara_attn_fwd",
     "tara_status_string", "tara_last_error", "tara_get_last_run_info",
@@ -33,6 +34,7 @@ __all__ = [
 TARA_SEG_TARGET, TARA_SEG_GUIDE, TARA_SEG_PICTURE, TARA_SEG_OTHER = 0, 1, 2, 3
 TARA_BF16, TARA_FP32 = 0, 1
 TARA_MODE_FUSED, TARA_MODE_PARTITIONED, TARA_MODE_THREE_TERM = 0, 1, 2
+TARA_MODE_DENSE_BIAS, TARA_MODE_FRAME_LOOP = 3, 4   # baselines for comparison
 TARA_MAX_PICTURES = 16
 TARA_MAX_BINDINGS = 4
 TARA_MAX_PARTITIONS = 64
@@ -155,7 +157,8 @@ def make_params(window: float = 0.20, falloff: float = 0.25, strength: float = 2
             p.picture_gain[j][i] = g
     p.softmax_scale = softmax_scale
     p.mode = {"fused": TARA_MODE_FUSED, "partitioned": TARA_MODE_PARTITIONED,
-              "three-term": TARA_MODE_THREE_TERM}[mode]
+              "three-term": TARA_MODE_THREE_TERM, "dense-bias": TARA_MODE_DENSE_BIAS,
+              "frame-loop": TARA_MODE_FRAME_LOOP}[mode]
     p.num_partitions = int(partitions)
     if bounds is not None:
         arr = (ctypes.c_int32 * len(bounds))(*[int(x) for x in bounds])

@@ -5,12 +5,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "tara_internal.h"
@@ -34,7 +36,7 @@ bool env_flag(const char* name) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tq, tk, kp, gt, ksum, vt, kmax, k8, ks, opart, lsepart, total;
+  size_t tq, tk, kp, gt, ksum, vt, kmax, k8, ks, dbias, opart, lsepart, total;
 };
 
 int npad_of(int N) { return (N + tara::kBlockK - 1) / tara::kBlockK * tara::kBlockK; }
@@ -43,7 +45,10 @@ int num_parts(const tara_params_t* p) {
   return p->mode == TARA_MODE_PARTITIONED ? p->num_partitions : p->mode == TARA_MODE_THREE_TERM ? 3 : 1;
 }
 
-bool has_partials(const tara_params_t* p) { return p->mode != TARA_MODE_FUSED; }
+// Modes whose attention passes write per-partition (O_p, LSE_p) for a merge.
+bool has_partials(const tara_params_t* p) {
+  return p->mode == TARA_MODE_PARTITIONED || p->mode == TARA_MODE_THREE_TERM;
+}
 
 // 8-bit Q.K: the bf16 path in fused mode only
 bool uses_qk8(tara_dtype_t dtype, const tara_params_t* p) { return p->qk8 && dtype == TARA_BF16; }
@@ -80,6 +85,7 @@ WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tar
     L.k8 = take((size_t)B * H * npad * D);
     L.ks = take((size_t)B * H * nkt * 4);
   }
+  if (p->mode == TARA_MODE_DENSE_BIAS) L.dbias = take((size_t)B * N * npad * 4);
   if (has_partials(p)) {
     const size_t parts = (size_t)num_parts(p);
     L.opart = take(parts * B * H * N * D * 4);
@@ -110,11 +116,13 @@ int check_params(const tara_params_t* p, int N) {
         if (!finite(p->picture_gain[j][i]) || !(p->picture_gain[j][i] > 0.0f))
           return fail(TARA_ERR_BAD_PARAM, "picture gains must be finite and > 0 (the rule adds m*ln(gain))");
   }
-  if (p->mode != TARA_MODE_FUSED && p->mode != TARA_MODE_PARTITIONED && p->mode != TARA_MODE_THREE_TERM)
-    return fail(TARA_ERR_BAD_PARAM, "mode must be TARA_MODE_FUSED, TARA_MODE_PARTITIONED or TARA_MODE_THREE_TERM");
-  if (p->mode == TARA_MODE_PARTITIONED) {
-    if (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS)
+  if (p->mode < TARA_MODE_FUSED || p->mode > TARA_MODE_FRAME_LOOP)
+    return fail(TARA_ERR_BAD_PARAM, "mode must be one of tara_mode_t");
+  if (p->mode == TARA_MODE_PARTITIONED || p->mode == TARA_MODE_FRAME_LOOP) {
+    if (p->mode == TARA_MODE_PARTITIONED && (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS))
       return fail(TARA_ERR_BAD_PARAM, "num_partitions must be in [1, 64]");
+    if (p->mode == TARA_MODE_FRAME_LOOP && (p->num_partitions < 1 || p->num_partitions > std::max(N, 1)))
+      return fail(TARA_ERR_BAD_PARAM, "FRAME_LOOP needs 1 <= num_partitions <= max(N, 1)");
     if (p->partition_bounds) {
       const int32_t* pb = p->partition_bounds;
       if (pb[0] != 0 || pb[p->num_partitions] != N)
@@ -210,6 +218,7 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D, cons
   if (p->mode == TARA_MODE_PARTITIONED && (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS))
     return (size_t)-1;
   if (!qk8_supported(dtype, p)) return (size_t)-1;
+  if (p->mode == TARA_MODE_DENSE_BIAS && dtype != TARA_BF16) return (size_t)-1;
   if (B == 0 || H == 0 || N == 0) return 0;
   return ws_layout_for(dtype, B, H, N, D, p).total;
 }
@@ -281,6 +290,8 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     return fail(TARA_ERR_BAD_SHAPE, "three-term mode supports N <= 2^20 (its key-tile lists live in LDS)");
   if (int st = check_params(p, N)) return st;
   if (!qk8_supported(dtype, p)) return fail(TARA_ERR_BAD_PARAM, "qk8 requires TARA_BF16 and TARA_MODE_FUSED");
+  if (p->mode == TARA_MODE_DENSE_BIAS && dtype != TARA_BF16)
+    return fail(TARA_ERR_BAD_PARAM, "TARA_MODE_DENSE_BIAS requires TARA_BF16");
   if (B == 0 || H == 0 || N == 0) {
     g_info = tara_run_info_t{p->mode, (int)dtype, 0, 0, num_parts(p), 0, tara::kBlockK, 0, 0};
     g_info_valid = true;
@@ -393,12 +404,30 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     for (int i = 0; i <= parts; ++i) aa.kr[i] = (int)((int64_t)N * i / parts);
   }
   const bool partitioned = has_partials(p);
+  aa.qr0 = 0;
+  aa.qr1 = N;
+  // query ranges, each its own launch of every pass (FRAME_LOOP: the caller's
+  // ranges; otherwise all rows at once)
+  std::vector<std::pair<int, int>> qranges;
+  if (p->mode == TARA_MODE_FRAME_LOOP) {
+    const int nr = p->num_partitions;
+    for (int i = 0; i < nr; ++i) {
+      const int r0 = p->partition_bounds ? p->partition_bounds[i] : (int)((int64_t)N * i / nr);
+      const int r1 = p->partition_bounds ? p->partition_bounds[i + 1] : (int)((int64_t)N * (i + 1) / nr);
+      if (r1 > r0) qranges.emplace_back(r0, r1);
+    }
+  } else {
+    qranges.emplace_back(0, N);
+  }
   // passes of the attention kernel: one fused pass, one pass over all key
   // ranges, or the three terms
   std::vector<int> passes;
-  if (p->mode == TARA_MODE_FUSED) passes = {tara::PASS_FUSED};
-  else if (p->mode == TARA_MODE_PARTITIONED) passes = {tara::PASS_RANGE};
-  else passes = {tara::PASS_TERM_A, tara::PASS_TERM_B, tara::PASS_TERM_C};
+  if (p->mode == TARA_MODE_PARTITIONED) passes = {tara::PASS_RANGE};
+  else if (p->mode == TARA_MODE_THREE_TERM) passes = {tara::PASS_TERM_A, tara::PASS_TERM_B, tara::PASS_TERM_C};
+  else passes = {tara::PASS_FUSED};
+  const bool dense = p->mode == TARA_MODE_DENSE_BIAS;
+  aa.dbias = dense ? reinterpret_cast<const float*>(ws + L.dbias) : nullptr;
+  const int variant = qk8 ? tara::ATTN_QK8 : dense ? tara::ATTN_DENSE_BIAS : tara::ATTN_PLAIN;
   int launches = 0;
   hipError_t e = tara::launch_meta(ma, stream);
   ++launches;
@@ -418,6 +447,11 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
       ++launches;
     }
   }
+  if (e == hipSuccess && dense) {
+    // the dense-bias baseline: every bias value written out before the attention pass
+    e = tara::launch_dense_bias(aa, const_cast<float*>(aa.dbias), stream);
+    ++launches;
+  }
   if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
 
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -433,19 +467,24 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   for (int pass : passes)
     if (pass != tara::PASS_FUSED && (!aa.opart || !aa.lsepart))
       return fail(TARA_ERR_HIP, "internal: a partition pass without its partial-output buffers");
-  for (int pass : passes) {
-    if (dtype == TARA_BF16) {
-      block_q = tara::attn_bf16_block_q(D);
-      aa.nqb = (N + block_q - 1) / block_q;
-      grid += tara::attn_bf16_grid(aa) * (pass == tara::PASS_RANGE ? parts : 1);
-      e = tara::launch_attn_bf16(aa, D, pass, qk8, stream);
-    } else {
-      block_q = tara::attn_f32_block_q(D);
-      aa.nqb = (N + block_q - 1) / block_q;
-      grid += aa.nqb * B * H * (pass == tara::PASS_RANGE ? parts : 1);
-      e = tara::launch_attn_f32(aa, D, pass, stream);
+  for (const auto& qrange : qranges) {
+    aa.qr0 = qrange.first;
+    aa.qr1 = qrange.second;
+    for (int pass : passes) {
+      if (dtype == TARA_BF16) {
+        block_q = tara::attn_bf16_block_q(D);
+        aa.nqb = (aa.qr1 - aa.qr0 + block_q - 1) / block_q;
+        grid += tara::attn_bf16_grid(aa) * (pass == tara::PASS_RANGE ? parts : 1);
+        e = tara::launch_attn_bf16(aa, D, pass, variant, stream);
+      } else {
+        block_q = tara::attn_f32_block_q(D);
+        aa.nqb = (aa.qr1 - aa.qr0 + block_q - 1) / block_q;
+        grid += aa.nqb * B * H * (pass == tara::PASS_RANGE ? parts : 1);
+        e = tara::launch_attn_f32(aa, D, pass, stream);
+      }
+      ++launches;
+      if (e != hipSuccess) break;
     }
-    ++launches;
     if (e != hipSuccess) break;
   }
   if (ev1) {
@@ -466,14 +505,19 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     ++launches;
     if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
   }
-  g_info = tara_run_info_t{p->mode, (int)dtype, bias_active, binding_active, parts, block_q, tara::kBlockK,
+  const int parts_info = p->mode == TARA_MODE_FRAME_LOOP ? (int)qranges.size() : parts;
+  g_info = tara_run_info_t{p->mode, (int)dtype, bias_active, binding_active, parts_info, block_q, tara::kBlockK,
                            grid, launches};
   g_info_valid = true;
   if (env_flag("TARA_LOG"))
     std::fprintf(stderr, "[tara] %s %s B=%d H=%d N=%d D=%d bias=%d binding=%d parts=%d grid=%d launches=%d\n",
-                 p->mode == TARA_MODE_THREE_TERM ? "three-term" : partitioned ? "partitioned" : "fused",
+                 p->mode == TARA_MODE_THREE_TERM   ? "three-term"
+                 : p->mode == TARA_MODE_DENSE_BIAS ? "dense-bias"
+                 : p->mode == TARA_MODE_FRAME_LOOP ? "frame-loop"
+                 : partitioned                     ? "partitioned"
+                                                   : "fused",
                  dtype == TARA_BF16 ? "bf16" : "fp32", B, H, N, D,
-                 (int)bias_active, (int)binding_active, parts, grid, launches);
+                 (int)bias_active, (int)binding_active, parts_info, grid, launches);
   return TARA_OK;
 }
 

@@ -26,6 +26,10 @@ constexpr int kMaxListTiles = 16384; // key tiles a three-term pass can list (N 
 //          C, guide times within the saturation gap of the workgroup's rows).
 enum : int { PASS_FUSED = 0, PASS_RANGE = 1, PASS_TERM_A = 2, PASS_TERM_B = 3, PASS_TERM_C = 4 };
 
+// Variants of the fused bf16 pass: plain; 8-bit Q.K; the dense-bias baseline
+// (bias read per element from a materialised [B][N][npad] fp32 tensor).
+enum : int { ATTN_PLAIN = 0, ATTN_QK8 = 1, ATTN_DENSE_BIAS = 2 };
+
 // Kind of a key tile, from the per-key encodings (see MetaArgs):
 //  PLAIN   no key of the tile can carry a bias term
 //  GUIDE   every key is a biased guide key; lo/hi = min/max time (s)
@@ -84,6 +88,7 @@ struct AttnArgs {
   float* opart;            // partitioned: O_p fp32 [P][B][H][N][D]
   float* lsepart;          // partitioned: LSE_p [P][B][H][N]
   int B, H, N, npad, nkt, nqb;
+  int qr0, qr1;            // query rows of this launch: [qr0, qr1) (all: 0, N); nqb covers them
   const float* tq;
   const float* tk;
   const int* kp;
@@ -93,6 +98,7 @@ struct AttnArgs {
   const float* kmax;       // bf16 path: [B*H][nkt] max |k| per key tile
   const uint8_t* k8;       // 8-bit Q.K: FP8 E4M3 keys [B*H][npad][D]
   const float* ks;         // 8-bit Q.K: power-of-two scale per key tile [B*H][nkt]
+  const float* dbias;      // dense-bias baseline: [B][N][npad] bias in log2 units
   float c;                 // softmax_scale * log2 e
   float sigma;             // sqrt(strength * log2 e) / falloff  (1/s)
   float w;                 // window * sigma
@@ -123,7 +129,8 @@ hipError_t launch_kquant(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, ui
 // Block of query rows per workgroup of the bf16 attention kernel.
 int attn_bf16_block_q(int D);
 int attn_bf16_grid(const AttnArgs& a);
-hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, bool qk8, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, int variant, hipStream_t s);
+hipError_t launch_dense_bias(const AttnArgs& a, float* out, hipStream_t s);
 int attn_f32_block_q(int D);
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int pass, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16_out, hipStream_t s);

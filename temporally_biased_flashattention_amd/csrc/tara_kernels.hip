@@ -616,12 +616,15 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
   }
 }
 
-template <int D, int NW, int PASS, bool Q8>
+template <int D, int NW, int PASS, bool Q8, bool DB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr bool PART = PASS != PASS_FUSED;   // writes one partition's (O_p, LSE_p)
   constexpr bool TERM = PASS >= PASS_TERM_A;  // visits a listed subset of the key tiles
   static_assert(!Q8 || PASS == PASS_FUSED, "8-bit Q.K is built for the fused pass");
+  // DB: the dense-bias baseline reads every logit's bias from a.dbias instead
+  // of computing it
+  static_assert(!DB || (PASS == PASS_FUSED && !Q8), "the dense-bias baseline is a fused bf16 pass");
   constexpr int BQ = NW * 32;              // query rows per workgroup
   constexpr int KROW = D + 8;              // padded LDS pitch of a bf16 K row (elements)
   // LDS pitch of a K row in bytes (FP8 rows: D bytes + a 16-byte pad)
@@ -661,9 +664,9 @@ void attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);   // uniform per wave
 
   // this lane's query row: column lq of the wave's S^T blocks
-  const int qrow = qblk * BQ + wave * 32 + lq;
-  const bool qvalid = qrow < N;
-  const int qr = qvalid ? qrow : N - 1;
+  const int qrow = a.qr0 + qblk * BQ + wave * 32 + lq;   // rows [qr0, qr1) of this launch
+  const bool qvalid = qrow < a.qr1;
+  const int qr = qvalid ? qrow : a.qr1 - 1;
   bf16x8 qf[Q8 ? 1 : NKK];
   i32x8 qf8[Q8 ? D / 64 : 1];
   float q_ss = 0.0f;                       // |q|^2 of the lane's share of the row
@@ -862,6 +865,20 @@ void attn_bf16_kernel(AttnArgs a) {
   const int voff_lane = lq * VROW + hh * 8;          // phase B reads V^T rows db*32 + lq
   // raw Q.K products to log2 units for a tile (cq: the row part; times the tile's scale)
   auto tile_mul = [&](float kscale) { return Q8 ? cq * kscale : a.c; };
+  // dense-bias baseline: this row of the bias tensor (pitch npad floats);
+  // bv[kb*4 + c2*2 + u] holds keys kb*32 + c2*16 + 8*hh + 4*u .. +3 of a tile
+  const float* dbq = DB ? a.dbias + ((int64_t)b * N + qr) * a.npad + 8 * hh : nullptr;
+  auto load_dbias = [&](f32x4 (&bv)[8], int kbase) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      bv[i] = *reinterpret_cast<const f32x4*>(dbq + kbase + (i >> 2) * 32 + ((i >> 1) & 1) * 16 + (i & 1) * 4);
+  };
+  auto apply_dbias = [&](f32x16 (&sv)[2], const f32x4 (&bv)[8], float cmul) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[kb][r] = fmaf(sv[kb][r], cmul, bv[kb * 4 + (r >> 2)][r & 3]);
+  };
 
   {
     // prologue: the first three tiles' K into K slots 0..2, the first two
@@ -890,7 +907,13 @@ void attn_bf16_kernel(AttnArgs a) {
     float brow;
     const bool lane_elem = tile_class_lane<PASS>(sm0, partial, qbiased, tq, gpic0, a, &brow);
     float cc = tile_mul(Q8 ? kscale_c[tile0] : 1.0f);
-    if (wave_any(lane_elem)) {
+    if constexpr (DB) {
+      f32x4 bv0[8];
+      load_dbias(bv0, kbase);
+      apply_dbias(x, bv0, cc);
+      brow = 0.0f;
+      cc = 1.0f;
+    } else if (wave_any(lane_elem)) {
       elem_bias<PASS>(x, kbase, hh, tq, (sm0.kind & KT_HAS_PICTURE) != 0, gtq, partial, k0, k1, tkb, kpb, a, cc);
       brow = 0.0f;
       cc = 1.0f;
@@ -944,6 +967,10 @@ void attn_bf16_kernel(AttnArgs a) {
     // a one-picture tile's bias is this row's gain-table entry for the
     // picture (read every tile, so no path waits on a pending load)
     const float gpic1 = gtq[max(sm1.pic, 0)];
+    // dense-bias baseline: the bias of tile t+1, loaded before K_{t+3} is
+    // staged so that waiting for it leaves that DMA in flight
+    f32x4 bv1[8];
+    if (DB && has1) load_dbias(bv1, tw1 * kBlockK);
     stage_k(tw3, s0);
     const int kbase1 = tw1 * kBlockK;
     const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
@@ -1005,7 +1032,11 @@ void attn_bf16_kernel(AttnArgs a) {
     float brow = 0.0f;
     float cc = tile_mul(kscale1);
     bool need_max = false;
-    if (has1) {
+    if (DB && has1) {
+      apply_dbias(sn, bv1, cc);
+      cc = 1.0f;
+      need_max = true;
+    } else if (has1) {
       const bool lane_elem = tile_class_lane<PASS>(sm1, partial1, qbiased, tq, gpic1, a, &brow);
       if (wave_any(lane_elem)) {
         elem_bias<PASS>(sn, kbase1, hh, tq, (sm1.kind & KT_HAS_PICTURE) != 0, gtq, partial1, k0, k1, tkb, kpb,
@@ -1140,26 +1171,74 @@ int attn_bf16_block_q(int) { return kWaves * 32; }
 int attn_bf16_grid(const AttnArgs& a) { return a.nqb * a.B * a.H; }
 
 template <int D>
-void launch_attn_bf16_d(const AttnArgs& a, int pass, bool qk8, dim3 grid, dim3 block, hipStream_t s) {
+void launch_attn_bf16_d(const AttnArgs& a, int pass, int variant, dim3 grid, dim3 block, hipStream_t s) {
   switch (pass) {
     case PASS_FUSED:
-      if (qk8) hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, true>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, false>), grid, block, 0, s, a);
+      if (variant == ATTN_QK8)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, true, false>), grid, block, 0, s, a);
+      else if (variant == ATTN_DENSE_BIAS)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, false, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, false, false>), grid, block, 0, s, a);
       break;
-    case PASS_RANGE: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE, false>), grid, block, 0, s, a); break;
-    case PASS_TERM_A: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_A, false>), grid, block, 0, s, a); break;
-    case PASS_TERM_B: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_B, false>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_C, false>), grid, block, 0, s, a); break;
+    case PASS_RANGE:
+      hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE, false, false>), grid, block, 0, s, a);
+      break;
+    case PASS_TERM_A:
+      hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_A, false, false>), grid, block, 0, s, a);
+      break;
+    case PASS_TERM_B:
+      hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_B, false, false>), grid, block, 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_C, false, false>), grid, block, 0, s, a);
+      break;
   }
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, bool qk8, hipStream_t s) {
-  // 8-bit Q.K exists for the one-pass form only (the host rejects the rest)
-  if (qk8 && pass != PASS_FUSED) return hipErrorInvalidValue;
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, int variant, hipStream_t s) {
+  // 8-bit Q.K and the dense-bias baseline exist for the one-pass form only
+  // (the host rejects the rest)
+  if (variant != ATTN_PLAIN && pass != PASS_FUSED) return hipErrorInvalidValue;
   dim3 grid(attn_bf16_grid(a), pass == PASS_RANGE ? a.nparts : 1);
   dim3 block(kWaves * 64);
-  if (D == 128) launch_attn_bf16_d<128>(a, pass, qk8, grid, block, s);
-  else launch_attn_bf16_d<64>(a, pass, qk8, grid, block, s);
+  if (D == 128) launch_attn_bf16_d<128>(a, pass, variant, grid, block, s);
+  else launch_attn_bf16_d<64>(a, pass, variant, grid, block, s);
+  return hipGetLastError();
+}
+
+// Dense-bias baseline: the bias of every (query, key) pair of batch element
+// blockIdx.z in log2 units, as the per-element path computes it (temporal
+// penalty of a biased target row against a biased guide key, plus the row's
+// summed log2 gain of a bound picture key), written as fp32 rows of npad keys;
+// keys at or past N get -inf. Four keys per thread.
+__global__ __launch_bounds__(256) void dense_bias_kernel(AttnArgs a, float* __restrict__ out) {
+  const int q = blockIdx.x, b = blockIdx.z;
+  const int k = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (k >= a.npad) return;
+  const int64_t qi = (int64_t)b * a.N + q;
+  const float tq = a.tq[qi];
+  const float* gq = a.gt + qi * a.npics;
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int kk = k + e;
+    float x = -INFINITY;
+    if (kk < a.N) {
+      const float tk = a.tk[(int64_t)b * a.npad + kk];
+      const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);   // NaN time -> 0
+      x = -fminf(dd * dd, a.cap2);
+      const int kp = a.kp[(int64_t)b * a.npad + kk];
+      if (kp >= 0) x += gq[kp];
+    }
+    r[e] = x;
+  }
+  *reinterpret_cast<f32x4*>(out + qi * a.npad + k) = r;
+}
+
+hipError_t launch_dense_bias(const AttnArgs& a, float* out, hipStream_t s) {
+  dim3 grid(a.N, (a.npad + 1023) / 1024, a.B);
+  hipLaunchKernelGGL(dense_bias_kernel, grid, dim3(256), 0, s, a, out);
   return hipGetLastError();
 }
 
@@ -1177,9 +1256,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int N = a.N;
   const int tid = threadIdx.x, sub = tid & 3;
-  const int qrow = blockIdx.x * kF32Queries + (tid >> 2);
-  const bool qvalid = qrow < N;
-  const int qr = qvalid ? qrow : N - 1;
+  const int qrow = a.qr0 + blockIdx.x * kF32Queries + (tid >> 2);   // rows [qr0, qr1) of this launch
+  const bool qvalid = qrow < a.qr1;
+  const int qr = qvalid ? qrow : a.qr1 - 1;
   const float* qp = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)qr * a.q_sn + sub * DL;
   const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh + sub * DL;
   const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh + sub * DL;
@@ -1267,7 +1346,7 @@ void launch_attn_f32_d(const AttnArgs& a, int pass, dim3 grid, dim3 block, hipSt
 }
 
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int pass, hipStream_t s) {
-  dim3 grid((a.N + kF32Queries - 1) / kF32Queries, a.B * a.H, pass == PASS_RANGE ? a.nparts : 1);
+  dim3 grid((a.qr1 - a.qr0 + kF32Queries - 1) / kF32Queries, a.B * a.H, pass == PASS_RANGE ? a.nparts : 1);
   dim3 block(256);
   if (D == 128) launch_attn_f32_d<128>(a, pass, grid, block, s);
   else launch_attn_f32_d<64>(a, pass, grid, block, s);

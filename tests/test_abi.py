@@ -90,6 +90,14 @@ def test_workspace_bytes():
         tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, p8)
     with pytest.raises(tara.TaraError):
         tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, tara.make_params(qk8=True, mode="three-term"))
+    # baselines: a dense fp32 bias [B][N][npad]; the frame loop needs nothing extra
+    pdb = tara.make_params(mode="dense-bias")
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, pdb) == meta + bf16_extra + _al(B * N * npad * 4)
+    with pytest.raises(tara.TaraError):
+        tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, pdb)
+    pfl = tara.make_params(mode="frame-loop", partitions=7)
+    assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, pfl) == meta + bf16_extra
+    assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, pfl) == meta
     with pytest.raises(tara.TaraError):
         tara.tara_workspace_bytes(tara.TARA_BF16, 1, 1, 10, 96, p)
     with pytest.raises(tara.TaraError):
@@ -155,6 +163,14 @@ def test_rejections(lib):
     assert call(lib, tara.make_params(qk8=True), dtype=tara.TARA_FP32, strides=(2 * 100 * 128, 100 * 128, 128)) == -6
     assert call(lib, tara.make_params(qk8=True, mode="partitioned", partitions=2)) == -6
     assert call(lib, tara.make_params(qk8=True, mode="three-term")) == -6
+    # baselines
+    assert call(lib, tara.make_params(mode="dense-bias"), dtype=tara.TARA_FP32,
+                strides=(2 * 100 * 128, 100 * 128, 128)) == -6
+    assert call(lib, tara.make_params(mode="frame-loop", partitions=0)) == -6
+    assert call(lib, tara.make_params(mode="frame-loop", partitions=101)) == -6          # > N
+    assert call(lib, tara.make_params(mode="frame-loop", partitions=2, bounds=(0, 60, 99))) == -6
+    assert call(lib, tara.make_params(mode="frame-loop", partitions=2, bounds=(0, 60, 40))) == -6
+    assert call(lib, tara.make_params(qk8=True, mode="frame-loop", partitions=2)) == -6
     # three-term passes keep their key-tile lists in LDS: N <= 2^20
     assert call(lib, tara.make_params(mode="three-term"), N=(1 << 20) + 64, H=1) == -2
 
