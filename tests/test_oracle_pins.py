@@ -524,7 +524,8 @@ def test_p12_fp8_e4m3_against_code_table():
 def test_p12_scales_and_dequantised_error():
     rng = np.random.default_rng(120)
     q = rng.standard_normal((300, 64)) * np.exp(rng.uniform(-6, 6, size=(300, 1)))
-    k = rng.standard_normal((300, 64)) * 3.0
+    # key tiles of 64 rows with magnitudes apart by up to e^8
+    k = rng.standard_normal((300, 64)) * 3.0 * np.repeat(np.exp(rng.uniform(-4, 4, size=(5, 1))), 64, axis=0)[:300]
     for row in q[:20]:
         s = oracle.pow2_scale(float(np.abs(row).max()))
         assert math.log2(s) == int(math.log2(s)) and 128.0 <= np.abs(row).max() / s < 256.0
@@ -538,6 +539,8 @@ def test_p12_scales_and_dequantised_error():
             # half an ulp: 2^-4 relative for normals, 2^-10 * scale below
             assert np.all(np.abs(bd - blk)[normal] <= np.abs(blk)[normal] * 2.0 ** -4)
             assert np.all(np.abs(bd - blk)[~normal] <= s * 2.0 ** -10)
+            # the largest element of every row / tile is a normal E4M3 value in [128, 256) * s
+            assert 128.0 <= np.abs(bd).max() / s <= 256.0
 
 
 # ----------------------------------------------------- planted mistakes fail a pin
@@ -553,7 +556,8 @@ def _pins_pass(golden_dir):
               lambda: test_p11_q0_closed_form_two_bindings(),
               lambda: test_p8_three_term_parts_merge_to_attention("defaults"),
               lambda: test_p12_fp8_e4m3_hand_worked(golden_dir),
-              lambda: test_p12_fp8_e4m3_against_code_table()]
+              lambda: test_p12_fp8_e4m3_against_code_table(),
+              lambda: test_p12_scales_and_dequantised_error()]
     for c in checks:
         try:
             c()
@@ -641,7 +645,18 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
         ulp = 2.0 ** (np.maximum(e, -6.0) - 3.0)
         return np.sign(x) * np.floor(a / ulp + 0.5) * ulp
 
-    mutants = [("penalty", no_square), ("penalty", no_window), ("bias_block", wrong_sign),
+    real_scale, real_deq = tor.pow2_scale, tor.qk8_dequantize
+
+    def scale_one_low(amax):
+        # largest magnitude lands in [64, 128): one bit of precision lost
+        return real_scale(amax) * 2.0
+
+    def per_tensor_k_scale(q, k, tile=64):
+        # one scale for all of K instead of one per key tile
+        return real_deq(q, k, tile=max(1, np.asarray(k).shape[0]))
+
+    mutants = [("pow2_scale", scale_one_low), ("qk8_dequantize", per_tensor_k_scale),
+               ("penalty", no_square), ("penalty", no_window), ("bias_block", wrong_sign),
                ("bias_block", swap_qk_roles), ("bias_block", log2_gain), ("attention_head", transposed_kv),
                ("bias_block", first_binding_only), ("bias_block", one_mask_plane),
                ("three_term_parts", correction_keeps_cap), ("fp8_e4m3_round", fp8_truncating),
@@ -649,6 +664,6 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
     for name, fn in mutants:
         with monkeypatch.context() as m:
             m.setattr(tor, name, fn)
-            if name in ("attention_head", "three_term_parts", "fp8_e4m3_round"):
+            if name in ("attention_head", "three_term_parts", "fp8_e4m3_round", "pow2_scale", "qk8_dequantize"):
                 m.setattr(oracle, name, fn)
             assert not _pins_pass(golden_dir), f"planted mistake {fn.__name__} went unnoticed"
