@@ -175,6 +175,9 @@ def main():
     kms = tara.tara_timing_read()
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
     info = tara.tara_get_last_run_info()
+    # the bf16 MFMA rate this machine sustains with nothing else to do, right after the timed steps
+    probe = tara.tara_probe_mfma_bf16(40000)
+    log(f"MFMA-only probe: {probe:.1f} TFLOP/s")
 
     if args.copy_calib_gib > 0:
         nb = int(args.copy_calib_gib * (1 << 30))
@@ -219,7 +222,9 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
                      "kernel_ms_avg": round(k_avg, 4), "launches_timed": len(kms),
-                     "flop_per_launch": flop},
+                     "flop_per_launch": flop,
+                     # back-to-back bf16 MFMAs on register operands, same box and clock
+                     "mfma_probe_tflops": round(probe, 1), "frac_of_mfma_probe": round(achieved / probe, 4)},
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")

@@ -243,6 +243,17 @@ int tara_get_last_run_info(tara_run_info_t* info);
 int tara_timing_enable(int on);
 int tara_timing_read(float* ms_out, int max, int* count);
 
+/* Measurement aid, not part of the attention path: runs a kernel made only of
+ * back-to-back bf16 MFMAs (v_mfma_f32_32x32x16_bf16) on register operands,
+ * two waves per SIMD on every CU, `iterations` rounds of four products per
+ * wave, on `stream` of the current device (one untimed launch, then one timed
+ * with HIP events), and stores the rate in *tflops. That rate is the MFMA
+ * ceiling the attention kernel meets on this device and clock, beside the
+ * nominal dense bf16 peak. Blocks until the launch completes. Returns
+ * TARA_ERR_NULL_POINTER for a NULL tflops, TARA_ERR_BAD_PARAM unless
+ * 1 <= iterations <= 2^24, TARA_ERR_HIP if a HIP call fails. */
+int tara_probe_mfma_bf16(int iterations, float* tflops, tara_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ __all__ = [
     "TaraError", "TaraLibraryMissing", "TaraParams", "TaraRunInfo",
     "tara_params_default", "make_params", "tara_workspace_bytes", "tara_attn_fwd",
     "tara_status_string", "tara_last_error", "tara_get_last_run_info",
-    "tara_timing_enable", "tara_timing_read", "attn_fwd", "library_path", "load_library",
+    "tara_timing_enable", "tara_timing_read", "tara_probe_mfma_bf16", "attn_fwd", "library_path",
+    "load_library",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -42,6 +43,7 @@ TARA_MAX_PARTITIONS = 64
 EXPORTED_SYMBOLS = (
     "tara_params_default", "tara_workspace_bytes", "tara_attn_fwd", "tara_status_string",
     "tara_last_error", "tara_get_last_run_info", "tara_timing_enable", "tara_timing_read",
+    "tara_probe_mfma_bf16",
 )
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -122,6 +124,8 @@ def load_library():
     lib.tara_timing_enable.restype = ctypes.c_int
     lib.tara_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.tara_timing_read.restype = ctypes.c_int
+    lib.tara_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]
+    lib.tara_probe_mfma_bf16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -250,6 +254,16 @@ def tara_timing_read(max_count: int = 4096):
     n = ctypes.c_int(0)
     _check(load_library().tara_timing_read(buf, max_count, ctypes.byref(n)))
     return [float(buf[i]) for i in range(n.value)]
+
+
+def tara_probe_mfma_bf16(iterations: int = 20000, stream=None) -> float:
+    """Rate (TFLOP/s) of a kernel of back-to-back bf16 MFMAs on the current device."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    out = ctypes.c_float(0.0)
+    _check(load_library().tara_probe_mfma_bf16(int(iterations), ctypes.byref(out), ctypes.c_void_p(stream.cuda_stream)))
+    return float(out.value)
 
 
 def attn_fwd(q, k, v, seg_type, token_time, picture_id=None, mask_weight=None,

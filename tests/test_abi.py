@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "tara.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tara_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tara_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -173,6 +173,13 @@ def test_rejections(lib):
     assert call(lib, tara.make_params(qk8=True, mode="frame-loop", partitions=2)) == -6
     # three-term passes keep their key-tile lists in LDS: N <= 2^20
     assert call(lib, tara.make_params(mode="three-term"), N=(1 << 20) + 64, H=1) == -2
+
+
+def test_probe_rejections(lib):
+    out = ctypes.c_float(0.0)
+    assert lib.tara_probe_mfma_bf16(100, None, None) == -1
+    assert lib.tara_probe_mfma_bf16(0, ctypes.byref(out), None) == -6
+    assert lib.tara_probe_mfma_bf16((1 << 24) + 1, ctypes.byref(out), None) == -6
 
 
 def test_messages(lib):

@@ -166,3 +166,12 @@ def test_segment_extremes():
         lay = ti.make_layout(7, (10, 10), (0, 0), 0, 0, 0)
         lay.seg[:] = seg
         check(q, k, v, lay, DEF, name)
+
+
+def test_mfma_probe_plausible():
+    """The MFMA-only probe the benchmark reports beside the kernel: a positive
+    rate below the nominal dense bf16 peak (2516.6 TFLOP/s)."""
+    import temporally_biased_flashattention_amd as tara
+    r = tara.tara_probe_mfma_bf16(20000)
+    log(f"MFMA-only probe: {r:.1f} TFLOP/s")
+    assert 500.0 < r < 2516.6
