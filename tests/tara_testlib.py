@@ -139,3 +139,21 @@ def sample_rows(lay: ti.Layout, n_random: int = 256, per_segment: int = 64, seed
             rows.update(int(x) for x in rng.choice(idx, size=min(per_segment, idx.size), replace=False))
     rows.update(range(max(0, n - tail), n))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def dequantized(q, k, heads=None, rows=None):
+    """fp32 copies of q and k ([B, H, N, D]) with the given heads' K tiles and
+    Q rows (all rows when rows is None) replaced by their 8-bit values
+    (exact in fp32: E4M3 values times powers of two)."""
+    qd, kd = q.float().clone(), k.float().clone()
+    hs = range(q.shape[1]) if heads is None else heads
+    for b in range(q.shape[0]):
+        for h in hs:
+            qs = q[b, h].float().numpy() if rows is None else q[b, h, rows].float().numpy()
+            a, c = oracle.qk8_dequantize(qs, k[b, h].float().numpy())
+            if rows is None:
+                qd[b, h] = torch.from_numpy(a).float()
+            else:
+                qd[b, h, rows] = torch.from_numpy(a).float()
+            kd[b, h] = torch.from_numpy(c).float()
+    return qd, kd

@@ -18,9 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import tara_inputs as ti
-from tara_testlib import compare, log, qkv_random, run_gpu, run_oracle, sample_rows
+from tara_testlib import compare, dequantized, log, qkv_random, run_gpu, run_oracle, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -31,24 +30,6 @@ BIND = ti.Params(window=0.10, falloff=0.40, strength=3.0, cap=8.0, binding=True,
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def dequantized(q, k, heads=None, rows=None):
-    """fp32 copies of q and k ([B, H, N, D]) with the given heads' K tiles and
-    Q rows (all rows when rows is None) replaced by their 8-bit values
-    (exact in fp32: E4M3 values times powers of two)."""
-    qd, kd = q.float().clone(), k.float().clone()
-    hs = range(q.shape[1]) if heads is None else heads
-    for b in range(q.shape[0]):
-        for h in hs:
-            qs = q[b, h].float().numpy() if rows is None else q[b, h, rows].float().numpy()
-            a, c = oracle.qk8_dequantize(qs, k[b, h].float().numpy())
-            if rows is None:
-                qd[b, h] = torch.from_numpy(a).float()
-            else:
-                qd[b, h, rows] = torch.from_numpy(a).float()
-            kd[b, h] = torch.from_numpy(c).float()
-    return qd, kd
 
 
 def logit_shift(q, k, qd, kd, scale, heads, rows):
