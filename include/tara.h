@@ -168,7 +168,8 @@ void tara_params_default(tara_params_t* p);
  * path, per-partition O/LSE in the partitioned and three-term modes, the FP8
  * keys with qk8 and the dense bias in DENSE_BIAS mode. Returns 0 for an empty
  * call (B, H or N == 0) and (size_t)-1 for arguments tara_attn_fwd would reject
- * (p == NULL, bad dtype or head dim, bad partition count). */
+ * (p == NULL, bad dtype or head dim, bad partition count, qk8 outside bf16
+ * fused mode, DENSE_BIAS with fp32). */
 size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
                             const tara_params_t* p);
 
