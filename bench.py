@@ -176,7 +176,7 @@ def main():
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
     info = tara.tara_get_last_run_info()
     # the bf16 MFMA rate this machine sustains with nothing else to do, right after the timed steps
-    probe = tara.tara_probe_mfma_bf16(40000)
+    probe = tara.tara_probe_mfma_bf16(400000)
     log(f"MFMA-only probe: {probe:.1f} TFLOP/s")
 
     if args.copy_calib_gib > 0:
