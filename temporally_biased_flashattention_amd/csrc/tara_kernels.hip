@@ -371,7 +371,7 @@ __device__ __forceinline__ void dma16(BufRange r, uint32_t voff, uint32_t soff, 
 // chunks) is staged by all NW waves: wave w takes blocks w, w + NW, ...
 // (PER_MAX DMAs for waves w < BLK % NW, PER_MIN, possibly 0, for the others). A lane whose
 // 16 bytes fall on a row's pad chunk re-reads chunk 0 of its row (never read
-// back). Buffer loads rather than global_load_lds: the latter is FLAT-encoded,
+// back; masking those lanes off costs more in branches than the bytes save). Buffer loads rather than global_load_lds: the latter is FLAT-encoded,
 // and while one is in flight the compiler cannot count LDS reads, so every
 // fragment wait would drain all of them.
 template <int ROWB, int DATA, int BLK, int NW>
@@ -984,13 +984,20 @@ void attn_bf16_kernel(AttnArgs a) {
     f32x16 sn[2];
     sn[0] = sn[1] = f32x16{};
     u32x4 pw[4];   // P_t as packed bf16 pairs: pw[kb*2 + c2] is the B operand of PV chunk (kb, c2)
-    auto exp_pair = [&](int i) {
-      // elements 2i, 2i+1 of the lane's 32 scores of tile t
+    // elements 2i, 2i+1 of the lane's 32 scores of tile t: exp2 in place,
+    // then (one MFMA slot later, off the exp latency) the bf16 pack
+    auto exp_only = [&](int i) {
       const int kb = i >> 3, r = (2 * i) & 15;
-      const float p0 = fast_exp2(x[kb][r]), p1 = fast_exp2(x[kb][r + 1]);
-      x[kb][r] = p0;
-      x[kb][r + 1] = p1;
-      pw[i >> 2][i & 3] = pack_bf16x2(p0, p1);
+      x[kb][r] = fast_exp2(x[kb][r]);
+      x[kb][r + 1] = fast_exp2(x[kb][r + 1]);
+    };
+    auto pack_pair = [&](int i) {
+      const int kb = i >> 3, r = (2 * i) & 15;
+      pw[i >> 2][i & 3] = pack_bf16x2(x[kb][r], x[kb][r + 1]);
+    };
+    auto exp_pair = [&](int i) {
+      exp_only(i);
+      pack_pair(i);
     };
     if constexpr (Q8) {
       // four (D 128) or two (D 64) FP8 products, the K fragments one ahead;
@@ -1018,11 +1025,14 @@ void attn_bf16_kernel(AttnArgs a) {
         if (j < NA) fr[j & 3] = kfrag<KROW>(kr0, j);
         else fr[j & 3] = vfrag<VROW, NDB>(vr0, j - NA);
         sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
-        if (i < 16) exp_pair(i);
+        if (i < 16) exp_only(i);
+        if (i >= 1 && i <= 16) pack_pair(i - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = NA; i < 16; ++i) exp_pair(i);
+      for (int i = NA; i < 16; ++i) exp_only(i);
+#pragma unroll
+      for (int i = NA < 17 ? NA - 1 : 16; i < 16; ++i) pack_pair(i);
     }
     // keep P_t in this block (the PV product that reads it follows the
     // bias-class branch)
