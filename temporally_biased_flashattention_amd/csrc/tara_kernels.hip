@@ -616,6 +616,11 @@ __device__ __forceinline__ void elem_bias(f32x16 (&s)[2], int kbase, int hh, flo
   }
 }
 
+template <int V>
+struct SlotIndex {
+  static constexpr int value = V;
+};
+
 template <int D, int NW, int PASS, bool Q8, bool DB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void attn_bf16_kernel(AttnArgs a) {
@@ -953,12 +958,14 @@ void attn_bf16_kernel(AttnArgs a) {
   // barrier), V^T of T_{t+2} into s2 after this step's barrier (T_{t-1}'s V^T
   // was last read before it). tw1..tw3 hold T_{t+1} .. T_{t+3}; a term pass
   // reads T_{t+4} from its LDS list one step ahead (tv4).
-  int s0 = 0;
   int tw1 = tile_at(1), tw2 = tile_at(2), tw3 = tile_at(3);
-  for (int t = 0; t < ntiles; ++t) {
+  // one step; the ring slots are compile-time constants (the loop below is
+  // unrolled by NS), so the slot arithmetic folds into the LDS offsets
+  auto step = [&](auto slot, int t) __attribute__((always_inline)) {
+    constexpr int s0 = decltype(slot)::value;
+    constexpr int s1 = (s0 + 1) % NS;
+    constexpr int s2 = (s0 + 2) % NS;
     const bool has1 = t + 1 < ntiles;
-    const int s1 = s0 + 1 == NS ? 0 : s0 + 1;
-    const int s2 = s1 + 1 == NS ? 0 : s1 + 1;
     int tv4 = 0;
     if (TERM) tv4 = tlist[min(t + 4, ntiles - 1)];
     const KeyTileSummary sm1 = sm_next;
@@ -1125,10 +1132,14 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int i = 0; i < NDB; ++i) o[i] *= alpha;
       m_used = m_new;
     }
-    s0 = s1;
     tw1 = tw2;
     tw2 = tw3;
     tw3 = TERM ? __builtin_amdgcn_readfirstlane(tv4) : min(kt0 + t + 4, kt1 - 1);
+  };
+  for (int t = 0; t < ntiles; t += NS) {
+    step(SlotIndex<0>{}, t);
+    if (t + 1 < ntiles) step(SlotIndex<1>{}, t + 1);
+    if (t + 2 < ntiles) step(SlotIndex<2>{}, t + 2);
   }
   // no DMA may still target this workgroup's LDS when it exits
   wait_vm<0>();
