@@ -175,3 +175,20 @@ def test_mfma_probe_plausible():
     r = tara.tara_probe_mfma_bf16(20000)
     log(f"MFMA-only probe: {r:.1f} TFLOP/s")
     assert 500.0 < r < 2516.6
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 0), (0, 2, 50), (1, 0, 50)])
+def test_empty_calls(shape):
+    """B, H or N == 0 is a valid empty call: OK status, nothing enqueued, run
+    info reports no launch."""
+    import temporally_biased_flashattention_amd as tara
+    B, H, N = shape
+    dev = "cuda"
+    q = torch.zeros(B, H, N, 128, dtype=torch.bfloat16, device=dev)
+    seg = torch.zeros(B, N, dtype=torch.uint8, device=dev)
+    tim = torch.zeros(B, N, dtype=torch.float32, device=dev)
+    for mode in ("fused", "partitioned", "three-term"):
+        o, l = tara.attn_fwd(q, q, q, seg, tim, params=tara.make_params(mode=mode, partitions=2 if mode == "partitioned" else 1))
+        torch.cuda.synchronize()
+        assert o.shape == (B, H, N, 128) and l.shape == (B, H, N)
+        assert tara.tara_get_last_run_info()["launches"] == 0
