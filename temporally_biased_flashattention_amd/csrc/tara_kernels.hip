@@ -981,6 +981,18 @@ void attn_bf16_kernel(AttnArgs a) {
     stage_k(tw3, s0);
     const int kbase1 = tw1 * kBlockK;
     const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
+    // bias class of tile t+1, worked out before phase A (it needs only the
+    // tile summary, the row and m, all known here): a per-row constant brow,
+    // or the per-element path if some lane needs it (cls_elem); cls_bound:
+    // every logit of the tile is <= |q| max|k| c + brow (Cauchy-Schwarz), and
+    // the exact row max is needed only when that bound could pass m + tau
+    float brow = 0.0f;
+    bool cls_elem = false, cls_bound = false;
+    if (!DB && has1) {
+      const bool lane_elem = tile_class_lane<PASS>(sm1, partial1, qbiased, tq, gpic1, a, &brow);
+      cls_elem = wave_any(lane_elem);
+      cls_bound = wave_any(fmaf(qn_c, kmax1, brow) > m_used + kRescaleTau);
+    }
     const __bf16* kr0 = KBUF(s1) + koff_lane;   // K_{t+1}
     const __bf16* vr0 = VBUF(s0) + voff_lane;   // V_t
     const __bf16* kn0 = KBUF(s2) + koff_lane;   // K_{t+2}
@@ -1045,8 +1057,7 @@ void attn_bf16_kernel(AttnArgs a) {
     // bias-class branch)
     asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]));
 
-    // bias class of tile t+1 (rare per-element path before phase B)
-    float brow = 0.0f;
+    // the rare per-element bias path of tile t+1, before phase B
     float cc = tile_mul(kscale1);
     bool need_max = false;
     if (DB && has1) {
@@ -1054,17 +1065,14 @@ void attn_bf16_kernel(AttnArgs a) {
       cc = 1.0f;
       need_max = true;
     } else if (has1) {
-      const bool lane_elem = tile_class_lane<PASS>(sm1, partial1, qbiased, tq, gpic1, a, &brow);
-      if (wave_any(lane_elem)) {
+      if (cls_elem) {
         elem_bias<PASS>(sn, kbase1, hh, tq, (sm1.kind & KT_HAS_PICTURE) != 0, gtq, partial1, k0, k1, tkb, kpb,
                         a, cc);
         brow = 0.0f;
         cc = 1.0f;
         need_max = true;
       } else {
-        // every logit of the tile is <= |q| max|k| c + brow (Cauchy-Schwarz);
-        // the exact row max is needed only when that bound could pass m + tau
-        need_max = wave_any(fmaf(qn_c, kmax1, brow) > m_used + kRescaleTau);
+        need_max = cls_bound;
       }
     }
     float m_new = m_used;
