@@ -346,6 +346,10 @@ constexpr int kGtPitch = kMaxPictures + 1;
 
 // LDS ring depth of the bf16 kernel (K and V^T tiles).
 constexpr int kStages = 3;
+// Key-loop start offset between consecutive query blocks, in key tiles
+// (measured: 4 halves the L2 misses of lockstep starts; 2, 3, 5, 6 and 8 do
+// less well).
+constexpr int kRotTiles = 4;
 
 // Key row held by S^T output row `r` of a 32-key block: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -798,10 +802,22 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
   // key tile visited at step i (steps past the end repeat the last tile: the
-  // ring slot it is staged into is free either way)
+  // ring slot it is staged into is free either way). The workgroups sharing an
+  // XCD's L2 run consecutive query blocks and stream the same K/V^T tiles; in
+  // lockstep they would all miss on a tile together, so each starts its loop
+  // kRotTiles tiles after the previous query block's (within 32 blocks): the
+  // first to reach a tile fetches it and the ones behind hit in L2. Any key
+  // order gives the same softmax; the rotation is fixed per query block, so
+  // results stay reproducible.
+  const int krot = (qblk & 31) * kRotTiles % ntiles;
+  // position in the pass's tile sequence (kt0 .. kt1-1, or the term list) of step i
+  auto step_pos = [&](int i) -> int {
+    const int j = min(i, ntiles - 1) + krot;
+    return j >= ntiles ? j - ntiles : j;
+  };
   auto tile_at = [&](int i) -> int {
-    if (TERM) return __builtin_amdgcn_readfirstlane((int)tlist[min(i, ntiles - 1)]);
-    return min(kt0 + i, kt1 - 1);
+    if (TERM) return __builtin_amdgcn_readfirstlane((int)tlist[step_pos(i)]);
+    return kt0 + step_pos(i);
   };
 
   // staging: buffer ranges over this head's K rows and V^T rows; per-lane
@@ -967,7 +983,7 @@ void attn_bf16_kernel(AttnArgs a) {
     constexpr int s2 = (s0 + 2) % NS;
     const bool has1 = t + 1 < ntiles;
     int tv4 = 0;
-    if (TERM) tv4 = tlist[min(t + 4, ntiles - 1)];
+    if (TERM) tv4 = tlist[step_pos(t + 4)];
     const KeyTileSummary sm1 = sm_next;
     const float kmax1 = kmax_next;
     const float kscale1 = kscale_next;
@@ -1142,7 +1158,7 @@ void attn_bf16_kernel(AttnArgs a) {
     }
     tw1 = tw2;
     tw2 = tw3;
-    tw3 = TERM ? __builtin_amdgcn_readfirstlane(tv4) : min(kt0 + t + 4, kt1 - 1);
+    tw3 = TERM ? __builtin_amdgcn_readfirstlane(tv4) : tile_at(t + 4);
   };
   for (int t = 0; t < ntiles; t += NS) {
     step(SlotIndex<0>{}, t);
