@@ -175,9 +175,12 @@ def main():
     kms = tara.tara_timing_read()
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
     info = tara.tara_get_last_run_info()
-    # the bf16 MFMA rate this machine sustains with nothing else to do, right after the timed steps
-    probe = tara.tara_probe_mfma_bf16(400000)
-    log(f"MFMA-only probe: {probe:.1f} TFLOP/s")
+    # the bf16 MFMA rates this box sustains with nothing else to do, right after the timed
+    # steps: on varied operands (power-limited, the practical ceiling on real data) and on
+    # constant operands (the top clock)
+    probe = tara.tara_probe_mfma_bf16(1000000, tara.TARA_PROBE_RANDOM)
+    probe_const = tara.tara_probe_mfma_bf16(400000, tara.TARA_PROBE_CONSTANT)
+    log(f"MFMA-only probes: {probe:.1f} TFLOP/s on varied operands, {probe_const:.1f} on constant operands")
 
     if args.copy_calib_gib > 0:
         nb = int(args.copy_calib_gib * (1 << 30))
@@ -223,8 +226,10 @@ def main():
                      "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
                      "kernel_ms_avg": round(k_avg, 4), "launches_timed": len(kms),
                      "flop_per_launch": flop,
-                     # back-to-back bf16 MFMAs on register operands, same box and clock
-                     "mfma_probe_tflops": round(probe, 1), "frac_of_mfma_probe": round(achieved / probe, 4)},
+                     # back-to-back bf16 MFMAs on register operands, same box: varied operands
+                     # (power-limited like the kernel's own products) and constant ones
+                     "mfma_probe_tflops": round(probe, 1), "frac_of_mfma_probe": round(achieved / probe, 4),
+                     "mfma_probe_constant_tflops": round(probe_const, 1)},
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")

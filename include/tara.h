@@ -244,16 +244,29 @@ int tara_get_last_run_info(tara_run_info_t* info);
 int tara_timing_enable(int on);
 int tara_timing_read(float* ms_out, int max, int* count);
 
+/* Operand kinds of tara_probe_mfma_bf16. */
+typedef enum {
+  TARA_PROBE_CONSTANT = 0, /* every product on the same two fragments: few bits
+                              toggle and the clock stays near its top, so this
+                              is the rate at which the matrix cores issue */
+  TARA_PROBE_RANDOM = 1    /* each wave cycles through 8 + 8 fragments of
+                              varied bf16 values, as real data does: the power
+                              limit sets the clock, so this is the practical
+                              ceiling for MFMA work on real data */
+} tara_probe_operands_t;
+
 /* Measurement aid, not part of the attention path: runs a kernel made only of
- * back-to-back bf16 MFMAs (v_mfma_f32_32x32x16_bf16) on register operands,
- * two waves per SIMD on every CU, `iterations` rounds of four products per
- * wave, on `stream` of the current device (one untimed launch, then one timed
- * with HIP events), and stores the rate in *tflops. That rate is the MFMA
- * ceiling the attention kernel meets on this device and clock, beside the
- * nominal dense bf16 peak. Blocks until the launch completes. Returns
- * TARA_ERR_NULL_POINTER for a NULL tflops, TARA_ERR_BAD_PARAM unless
- * 1 <= iterations <= 2^24, TARA_ERR_HIP if a HIP call fails. */
-int tara_probe_mfma_bf16(int iterations, float* tflops, tara_stream_t stream);
+ * back-to-back bf16 MFMAs (v_mfma_f32_32x32x16_bf16) on register operands of
+ * the given kind (a tara_probe_operands_t), two waves per SIMD on every CU,
+ * `iterations` rounds of four products per wave, on `stream` of the current
+ * device (one untimed launch, then one timed with HIP events), and stores the
+ * rate in *tflops. Those rates are the MFMA ceilings the attention kernel
+ * meets on this device, beside the nominal dense bf16 peak. Blocks until the
+ * launch completes. Returns TARA_ERR_NULL_POINTER for a NULL tflops,
+ * TARA_ERR_BAD_PARAM unless 1 <= iterations <= 2^24 and `operands` is one of
+ * the kinds (checked before any device work), TARA_ERR_HIP if a HIP call
+ * fails. */
+int tara_probe_mfma_bf16(int iterations, int operands, float* tflops, tara_stream_t stream);
 
 #ifdef __cplusplus
 }

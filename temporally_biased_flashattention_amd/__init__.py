@@ -124,7 +124,7 @@ def load_library():
     lib.tara_timing_enable.restype = ctypes.c_int
     lib.tara_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.tara_timing_read.restype = ctypes.c_int
-    lib.tara_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]
+    lib.tara_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]
     lib.tara_probe_mfma_bf16.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -256,13 +256,20 @@ def tara_timing_read(max_count: int = 4096):
     return [float(buf[i]) for i in range(n.value)]
 
 
-def tara_probe_mfma_bf16(iterations: int = 20000, stream=None) -> float:
-    """Rate (TFLOP/s) of a kernel of back-to-back bf16 MFMAs on the current device."""
+TARA_PROBE_CONSTANT = 0
+TARA_PROBE_RANDOM = 1
+
+
+def tara_probe_mfma_bf16(iterations: int = 20000, operands: int = TARA_PROBE_RANDOM, stream=None) -> float:
+    """Rate (TFLOP/s) of a kernel of back-to-back bf16 MFMAs on the current
+    device, on constant (TARA_PROBE_CONSTANT) or varied (TARA_PROBE_RANDOM)
+    register operands."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream()
     out = ctypes.c_float(0.0)
-    _check(load_library().tara_probe_mfma_bf16(int(iterations), ctypes.byref(out), ctypes.c_void_p(stream.cuda_stream)))
+    _check(load_library().tara_probe_mfma_bf16(int(iterations), int(operands), ctypes.byref(out),
+                                               ctypes.c_void_p(stream.cuda_stream)))
     return float(out.value)
 
 

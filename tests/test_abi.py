@@ -177,9 +177,11 @@ def test_rejections(lib):
 
 def test_probe_rejections(lib):
     out = ctypes.c_float(0.0)
-    assert lib.tara_probe_mfma_bf16(100, None, None) == -1
-    assert lib.tara_probe_mfma_bf16(0, ctypes.byref(out), None) == -6
-    assert lib.tara_probe_mfma_bf16((1 << 24) + 1, ctypes.byref(out), None) == -6
+    assert lib.tara_probe_mfma_bf16(100, 1, None, None) == -1
+    assert lib.tara_probe_mfma_bf16(0, 1, ctypes.byref(out), None) == -6
+    assert lib.tara_probe_mfma_bf16((1 << 24) + 1, 0, ctypes.byref(out), None) == -6
+    assert lib.tara_probe_mfma_bf16(100, 2, ctypes.byref(out), None) == -6
+    assert lib.tara_probe_mfma_bf16(100, -1, ctypes.byref(out), None) == -6
 
 
 def test_messages(lib):

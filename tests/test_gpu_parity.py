@@ -168,12 +168,14 @@ def test_segment_extremes():
         check(q, k, v, lay, DEF, name)
 
 
-def test_mfma_probe_plausible():
-    """The MFMA-only probe the benchmark reports beside the kernel: a positive
-    rate below the nominal dense bf16 peak (2516.6 TFLOP/s)."""
+@pytest.mark.parametrize("operands", ["constant", "random"])
+def test_mfma_probe_plausible(operands):
+    """The MFMA-only probes the benchmark reports beside the kernel: positive
+    rates below the nominal dense bf16 peak (2516.6 TFLOP/s)."""
     import temporally_biased_flashattention_amd as tara
-    r = tara.tara_probe_mfma_bf16(20000)
-    log(f"MFMA-only probe: {r:.1f} TFLOP/s")
+    kind = tara.TARA_PROBE_CONSTANT if operands == "constant" else tara.TARA_PROBE_RANDOM
+    r = tara.tara_probe_mfma_bf16(20000, kind)
+    log(f"MFMA-only probe, {operands} operands: {r:.1f} TFLOP/s")
     assert 500.0 < r < 2516.6
 
 
