@@ -23,7 +23,7 @@ from typing import Optional, Sequence
 __all__ = [
     "TARA_SEG_TARGET", "TARA_SEG_GUIDE", "TARA_SEG_PICTURE", "TARA_SEG_OTHER",
     "TARA_BF16", "TARA_FP32", "TARA_MODE_FUSED", "TARA_MODE_PARTITIONED", "TARA_MODE_THREE_TERM",
-    "TARA_MODE_DENSE_BIAS", "TARA_MODE_FRAME_LOOP",
+    "TARA_MODE_DENSE_BIAS", "TARA_MODE_FRAME_LOOP", "TARA_PROBE_CONSTANT", "TARA_PROBE_RANDOM",
     "TaraError", "TaraLibraryMissing", "TaraParams", "TaraRunInfo",
     "tara_params_default", "make_params", "tara_workspace_bytes", "tara_attn_fwd",
     "tara_status_string", "tara_last_error", "tara_get_last_run_info",
