@@ -454,19 +454,21 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   }
   if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
 
+  for (int pass : passes)
+    if (pass != tara::PASS_FUSED && (!aa.opart || !aa.lsepart))
+      return fail(TARA_ERR_HIP, "internal: a partition pass without its partial-output buffers");
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
     if (g_timing) {
-      if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
+      if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) {
+        if (ev0) (void)hipEventDestroy(ev0);
         return fail(TARA_ERR_HIP, "hipEventCreate failed");
+      }
       (void)hipEventRecord(ev0, stream);
     }
   }
   int grid = 0, block_q = 0;
-  for (int pass : passes)
-    if (pass != tara::PASS_FUSED && (!aa.opart || !aa.lsepart))
-      return fail(TARA_ERR_HIP, "internal: a partition pass without its partial-output buffers");
   for (const auto& qrange : qranges) {
     aa.qr0 = qrange.first;
     aa.qr1 = qrange.second;
