@@ -11,10 +11,16 @@
 // Kernels
 //   meta_kernel        per-token encodings + per-64-key tile summaries  (O(N))
 //   vtranspose_kernel  V [B,H,N,D] -> V^T [B*H][D][npad], keys contiguous (HBM-bound)
+//   knorm_kernel       max |k| per 64-key tile (the row-max bound of the bf16 pass)
+//   kquant_kernel      8-bit Q.K: K in FP8 E4M3 with one power-of-two scale per
+//                      tile, plus the tile norms
+//   dense_bias_kernel  the dense-bias baseline: every logit's bias written out
 //   attn_bf16_kernel   the fused pass: bf16 MFMA S^T = K Q^T, bias, online
 //                      softmax, MFMA O^T += V^T P^T, one workgroup per block
 //                      of query rows of one (batch, head), streaming all key
-//                      tiles of its key range through LDS
+//                      tiles of its key range through LDS; its variants serve
+//                      key-range partitions, the three term passes, 8-bit Q.K
+//                      and the dense-bias baseline
 //   attn_f32_kernel    fp32 inputs: same arithmetic with FMA (correctness path)
 //   merge_kernel       exact LSE merge of per-partition (O_p, LSE_p)
 //
