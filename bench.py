@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 # Q.K at the FP8 rate and P.V at the bf16 rate, equal FLOP each
 PEAK_QK8_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
-PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 FLOP/clk/CU), the fp32 path's bound
 METRIC = "TARA attention TFLOP/s and % of bf16 MFMA peak at 107,126 tok × 56 heads"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_headline_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "temporally_biased_flashattention_amd", "csrc", "tara_kernels.hip")
@@ -57,15 +57,16 @@ def workload(name):
     return ti.config(cid)
 
 
-def measured_traffic(per_launch_flop_unit):
+def measured_traffic(workload_name):
     """HBM bytes per attention launch from the committed counter summary, if
-    it was taken on the current kernel source (else None)."""
+    it was taken on the current kernel source and this workload and mode
+    (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha() or t.get("workload") != workload_name:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -197,8 +198,10 @@ def main():
     value = flop / (ms_step / 1e3) / 1e12
     k_avg = sum(kms) / len(kms) if kms else float("nan")
     achieved = flop / (k_avg / 1e3) / 1e12
-    traffic = None if args.qk8 else measured_traffic(flop)
-    peak = PEAK_QK8_TFLOPS if args.qk8 else PEAK_BF16_TFLOPS
+    traffic = None if args.qk8 else measured_traffic(f"{cfg.name} {args.mode}")
+    # fp32 inputs run the FMA path: bound by the fp32 vector ALUs, not the MFMA units
+    fp32_path = cfg.dtype != "bf16"
+    peak = PEAK_FP32_VALU_TFLOPS if fp32_path else PEAK_QK8_TFLOPS if args.qk8 else PEAK_BF16_TFLOPS
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -221,7 +224,7 @@ def main():
                                 "binding": cfg.params.binding, "gains": list(cfg.params.gains),
                                 "chained_gains": [list(c) for c in cfg.params.chained]},
                    "block_q": info.get("block_q"), "block_k": info.get("block_k"), "grid": info.get("grid")},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
+        "roofline": {"bound": "alu" if fp32_path else "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
                      "kernel_ms_avg": round(k_avg, 4), "launches_timed": len(kms),
