@@ -379,11 +379,12 @@ __device__ __forceinline__ void dma16(BufRange r, uint32_t voff, uint32_t soff, 
 // writes 64 lanes x 16 bytes contiguously at a uniform LDS address. A padded
 // tile of BLK whole 1-KB blocks (rows of ROWB bytes holding DATA 16-byte data
 // chunks) is staged by all NW waves: wave w takes blocks w, w + NW, ...
-// (PER_MAX DMAs for waves w < BLK % NW, PER_MIN, possibly 0, for the others). A lane whose
-// 16 bytes fall on a row's pad chunk re-reads chunk 0 of its row (never read
-// back; masking those lanes off costs more in branches than the bytes save). Buffer loads rather than global_load_lds: the latter is FLAT-encoded,
-// and while one is in flight the compiler cannot count LDS reads, so every
-// fragment wait would drain all of them.
+// (PER_MAX DMAs for waves w < BLK % NW, PER_MIN, possibly 0, for the others).
+// A lane whose 16 bytes fall on a row's pad chunk re-reads chunk 0 of its row
+// (never read back; masking those lanes off costs more in branches than the
+// bytes save). Buffer loads rather than global_load_lds: the latter is
+// FLAT-encoded, and while one is in flight the compiler cannot count LDS
+// reads, so every fragment wait would drain all of them.
 template <int ROWB, int DATA, int BLK, int NW>
 struct TileDma {
   static constexpr int PER_MIN = BLK / NW;
