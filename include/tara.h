@@ -98,7 +98,8 @@ typedef enum {
   TARA_ERR_BAD_SHAPE = -2,          /* B, H or N negative or too large */
   TARA_ERR_UNSUPPORTED_DTYPE = -3,  /* dtype not TARA_BF16 / TARA_FP32 */
   TARA_ERR_UNSUPPORTED_HEAD_DIM = -4, /* D not 64 or 128 */
-  TARA_ERR_BAD_STRIDE = -5,         /* base or stride not 16-byte aligned, or negative */
+  TARA_ERR_BAD_STRIDE = -5,         /* base or stride not 16-byte aligned, or negative, or (bf16)
+                                       too large for 32-bit tile offsets (see tara_attn_fwd) */
   TARA_ERR_BAD_PARAM = -6,          /* a control out of range (see tara_params_t) */
   TARA_ERR_WORKSPACE = -7,          /* workspace NULL or smaller than tara_workspace_bytes() */
   TARA_ERR_BAD_METADATA = -8,       /* only with TARA_VALIDATE=1: metadata out of range */
@@ -178,7 +179,10 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
  *  q, k, v  device, dtype elements, logical shape [B][H][N][D], element
  *           (b,h,n,d) at base + b*str[0] + h*str[1] + n*str[2] + d (d contiguous).
  *           Base addresses 16-byte aligned; every stride a multiple of
- *           16 bytes / sizeof(element) and >= 0.
+ *           16 bytes / sizeof(element) and >= 0. bf16: the kernel addresses
+ *           one head's key rows with 32-bit byte offsets, so k_str[2] * 2 *
+ *           Npad and D * Npad * 2 (Npad: N rounded up to 64) must be < 2^31
+ *           (else TARA_ERR_BAD_STRIDE).
  *  o        device, same dtype and layout rules (strides o_str); fully written.
  *  lse      device fp32 [B][H][N] contiguous, natural log; fully written.
  *  dtype    TARA_BF16 (bf16 in and out, fp32 accumulation) or TARA_FP32.

@@ -305,11 +305,13 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (int st = check_strides("v", v, v_str, esize)) return st;
   if (int st = check_strides("o", o, o_str, esize)) return st;
   if ((reinterpret_cast<uintptr_t>(lse) & 3) != 0) return fail(TARA_ERR_BAD_STRIDE, "lse is not 4-byte aligned");
-  // the bf16 kernel stages key tiles with 32-bit byte offsets: 64 rows of K and
-  // D rows of the key-contiguous V copy must stay below 2^31 bytes
-  if (dtype == TARA_BF16 && ((int64_t)k_str[2] * 2 * tara::kBlockK >= (int64_t(1) << 31) ||
+  // the bf16 kernel stages key tiles with 32-bit byte offsets from one head's
+  // K rows and from its rows of the key-contiguous V copy: N (padded to whole
+  // tiles) rows of K at its row stride, and D rows of that copy, must each
+  // span less than 2^31 bytes
+  if (dtype == TARA_BF16 && ((int64_t)k_str[2] * 2 * npad_of(N) >= (int64_t(1) << 31) ||
                              (int64_t)D * npad_of(N) * 2 >= (int64_t(1) << 31)))
-    return fail(TARA_ERR_BAD_STRIDE, "K row stride or N too large for the bf16 kernel's 32-bit tile offsets");
+    return fail(TARA_ERR_BAD_STRIDE, "K row stride x N or D x N too large for the bf16 kernel's 32-bit tile offsets");
 
   // derived constants, in double then rounded once to fp32
   const double log2e = 1.4426950408889634;

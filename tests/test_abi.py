@@ -130,6 +130,14 @@ def test_rejections(lib):
     assert call(lib, P(), q=FAKE + 8) == -5                      # base not 16-byte aligned
     assert call(lib, P(), strides=(1000 * 128, 100 * 128, 130)) == -5   # row stride not x8
     assert call(lib, P(), dtype=tara.TARA_FP32, strides=(800, 400, 6)) == -5
+    # bf16: one head's key rows are addressed with 32-bit byte offsets
+    # (row stride x N padded to 64, and D x N padded, below 2^31 bytes)
+    # (ws_bytes=10: a call that passes these checks stops at the workspace check)
+    n = 1 << 20
+    assert call(lib, P(), H=8, N=n, strides=(n * 8 * 128, 128, 8 * 128), ws_bytes=10) == -5   # BNHD, 8 heads: 2^31
+    assert call(lib, P(), H=7, N=n, strides=(n * 7 * 128, 128, 7 * 128), ws_bytes=10) == -7   # 7 heads: below
+    assert call(lib, P(), N=(1 << 23) - 10, H=1, ws_bytes=10) == -5                          # D x Npad x 2 = 2^31
+    assert call(lib, P(), N=(1 << 23) - 64, H=1, ws_bytes=10) == -7                          # one tile less
     assert call(lib, P(), ws_bytes=10) == -7
     assert call(lib, P(), ws=0) == -7
     assert call(lib, P(), ws=FAKE + 64) == -7                    # not 256-byte aligned
