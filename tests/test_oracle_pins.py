@@ -655,7 +655,42 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
         # one scale for all of K instead of one per key tile
         return real_deq(q, k, tile=max(1, np.asarray(k).shape[0]))
 
+    def no_cap(dt, w, f, s, c):
+        # the quadratic never saturates
+        x = np.maximum(np.abs(np.asarray(dt, np.float64)) - w, 0.0) / f
+        return s * x * x
+
+    def guide_rows_biased_too(seg_q, tq, mq, seg_k, tk, pk, params):
+        # guide queries treated like target queries
+        return real_bias(np.where(np.asarray(seg_q) == tor.GUIDE, tor.TARGET, seg_q), tq, mq, seg_k, tk, pk, params)
+
+    def binding_on_every_row(seg_q, tq, mq, seg_k, tk, pk, params):
+        # the binding term added for every query row, not only target rows
+        b = real_bias(seg_q, tq, mq, seg_k, tk, pk, params)
+        if not params.binding:
+            return b
+        seg_q = np.asarray(seg_q)
+        other = seg_q != tor.TARGET
+        if not other.any():
+            return b
+        only_binding = ti.Params(params.window, params.falloff, 0.0, params.cap, params.binding, params.gains,
+                                 chained=params.chained)
+        nb = getattr(params, "num_bindings", 1)
+        ones = None if mq is None else np.ones((nb, seg_q.shape[0]))
+        ball = real_bias(np.full_like(seg_q, tor.TARGET), tq, ones, seg_k, tk, pk, only_binding)
+        return b + np.where(other[:, None], ball, 0.0)
+
+    def bias_scaled_like_logits(*a, **kw):
+        # the bias multiplied by the softmax scale of a 64-wide head
+        return real_bias(*a, **kw) * 0.125
+
+    def mask_ignored(seg_q, tq, mq, seg_k, tk, pk, params):
+        # m = 1 on every target query whatever the mask says
+        return real_bias(seg_q, tq, None, seg_k, tk, pk, params)
+
     mutants = [("pow2_scale", scale_one_low), ("qk8_dequantize", per_tensor_k_scale),
+               ("penalty", no_cap), ("bias_block", guide_rows_biased_too), ("bias_block", binding_on_every_row),
+               ("bias_block", bias_scaled_like_logits), ("bias_block", mask_ignored),
                ("penalty", no_square), ("penalty", no_window), ("bias_block", wrong_sign),
                ("bias_block", swap_qk_roles), ("bias_block", log2_gain), ("attention_head", transposed_kv),
                ("bias_block", first_binding_only), ("bias_block", one_mask_plane),
