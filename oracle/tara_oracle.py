@@ -33,6 +33,14 @@ Readings where the pages are silent (each listed in the design notes):
   * a key range restricts the softmax to keys [k0, k1) (one partition).
 
 Segment codes are those of the C ABI: 0 target, 1 guide, 2 picture, 3 other.
+
+What pins it (tests/test_oracle_pins.py, P1-P12): closed forms of the
+penalty and of Q = 0 attention, reduction to a library softmax attention
+when the bias is off, brute force on tiny inputs, the partition merge and
+three-term identities, invariances, monotonicity, chained bindings, and the
+8-bit rounding against the format's definition; planted mistakes must fail
+them. Absolute O and LSE on random inputs are pinned only through these: the
+pages print no attention outputs (parity unpinned beyond the pins).
 """
 from __future__ import annotations
 
