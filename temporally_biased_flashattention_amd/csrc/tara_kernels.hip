@@ -1406,46 +1406,94 @@ hipError_t launch_attn_f32(const AttnArgs& a, int D, int pass, hipStream_t s) {
 }
 
 // --------------------------------------------------------------- LSE merge
-// One thread per (row, 4 consecutive dims).
-template <bool BF16_OUT>
+// One thread per (row, 8 consecutive dims): LSE = M + ln sum_p e^(LSE_p - M),
+// O = sum_p e^(LSE_p - LSE) O_p (a row whose partitions are all empty gets O
+// 0 and LSE -inf). NP > 0: exactly NP partitions, unrolled so that every load
+// of the row is in flight at once; NP == 0: a.nparts, looped.
+template <bool BF16_OUT, int NP>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int dq = a.D / 4;
+  const int dq = a.D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (gid >= rows * dq) return;
-  const int d4 = (int)(gid % dq);
+  const int d8 = (int)(gid % dq);
   const int64_t row = gid / dq;                   // (b*H + h)*N + n
   const int n = (int)(row % a.N);
   const int64_t bh = row / a.N;
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  float mx = -INFINITY;
-  for (int p = 0; p < a.nparts; ++p) mx = fmaxf(mx, a.lsepart[(int64_t)p * rows + row]);
-  float ssum = 0.0f;
-  for (int p = 0; p < a.nparts; ++p) ssum += expf(a.lsepart[(int64_t)p * rows + row] - mx);
-  const float lse = mx + logf(ssum);
-  f32x4 acc = f32x4{};
-  for (int p = 0; p < a.nparts; ++p) {
-    const float w = expf(a.lsepart[(int64_t)p * rows + row] - lse);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.opart + ((int64_t)p * rows + row) * a.D + d4 * 4);
-    acc += w * x;
-  }
-  const int64_t oo = b * a.o_sb + h * a.o_sh + (int64_t)n * a.o_sn + d4 * 4;
-  if (BF16_OUT) {
-    bf16x4 y;
+  const int np = NP > 0 ? NP : a.nparts;
+  f32x4 acc0 = f32x4{}, acc1 = f32x4{};
+  float lse = -INFINITY;
+  if constexpr (NP > 0) {
+    float l[NP];
+    f32x4 x0[NP], x1[NP];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = (__bf16)acc[i];
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o) + oo) = y;
+    for (int p = 0; p < NP; ++p) {
+      l[p] = a.lsepart[(int64_t)p * rows + row];
+      const float* op = a.opart + ((int64_t)p * rows + row) * a.D + d8 * 8;
+      x0[p] = *reinterpret_cast<const f32x4*>(op);
+      x1[p] = *reinterpret_cast<const f32x4*>(op + 4);
+    }
+    float mx = l[0];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) mx = fmaxf(mx, l[p]);
+    if (mx != -INFINITY) {
+      float ssum = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) ssum += expf(l[p] - mx);
+      lse = mx + logf(ssum);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const float w = expf(l[p] - lse);
+        acc0 += w * x0[p];
+        acc1 += w * x1[p];
+      }
+    }
   } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + oo) = acc;
+    float mx = -INFINITY;
+    for (int p = 0; p < np; ++p) mx = fmaxf(mx, a.lsepart[(int64_t)p * rows + row]);
+    if (mx != -INFINITY) {
+      float ssum = 0.0f;
+      for (int p = 0; p < np; ++p) ssum += expf(a.lsepart[(int64_t)p * rows + row] - mx);
+      lse = mx + logf(ssum);
+      for (int p = 0; p < np; ++p) {
+        const float w = expf(a.lsepart[(int64_t)p * rows + row] - lse);
+        const float* op = a.opart + ((int64_t)p * rows + row) * a.D + d8 * 8;
+        acc0 += w * *reinterpret_cast<const f32x4*>(op);
+        acc1 += w * *reinterpret_cast<const f32x4*>(op + 4);
+      }
+    }
   }
-  if (d4 == 0) a.lse[row] = lse;
+  const int64_t oo = b * a.o_sb + h * a.o_sh + (int64_t)n * a.o_sn + d8 * 8;
+  if (BF16_OUT) {
+    bf16x8 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = (__bf16)acc0[i];
+      y[i + 4] = (__bf16)acc1[i];
+    }
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.o) + oo) = y;
+  } else {
+    float* o = static_cast<float*>(a.o) + oo;
+    *reinterpret_cast<f32x4*>(o) = acc0;
+    *reinterpret_cast<f32x4*>(o + 4) = acc1;
+  }
+  if (d8 == 0) a.lse[row] = lse;
+}
+
+template <bool BF16_OUT>
+void launch_merge_np(const MergeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.nparts == 2) hipLaunchKernelGGL((merge_kernel<BF16_OUT, 2>), grid, dim3(256), 0, s, a);
+  else if (a.nparts == 3) hipLaunchKernelGGL((merge_kernel<BF16_OUT, 3>), grid, dim3(256), 0, s, a);
+  else if (a.nparts == 4) hipLaunchKernelGGL((merge_kernel<BF16_OUT, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((merge_kernel<BF16_OUT, 0>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool bf16_out, hipStream_t s) {
-  const int64_t total = (int64_t)a.B * a.H * a.N * (a.D / 4);
+  const int64_t total = (int64_t)a.B * a.H * a.N * (a.D / 8);
   dim3 grid((unsigned)((total + 255) / 256));
-  if (bf16_out) hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(256), 0, s, a);
+  if (bf16_out) launch_merge_np<true>(a, grid, s);
+  else launch_merge_np<false>(a, grid, s);
   return hipGetLastError();
 }
 
