@@ -209,31 +209,35 @@ hipError_t launch_vtranspose(const __bf16* v, int64_t sb, int64_t sh, int64_t sn
 
 // ------------------------------------------------------ key-tile norm bound
 // kmax[b*H + h][t] = max |k_n| over the 64 keys of tile t (rows past N repeat
-// row N-1, as the attention kernel's staging does). 256 threads per tile: four
-// adjacent threads read one row's D/4 contiguous elements (coalesced), the
-// row's sum of squares is combined across them, then the max over the rows.
+// row N-1, as the attention kernel's staging does). 256 threads per tile; each
+// wave reads 16 rows, four per load instruction: lane l takes 16 bytes of row
+// l / (D/8) at chunk l % (D/8), so one instruction reads whole rows
+// contiguously. A row's sum of squares is combined across its D/8 lanes, then
+// the max is taken over the rows.
 __global__ __launch_bounds__(256) void knorm_kernel(const __bf16* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
                                                     int H, int N, int D, int nkt, float* __restrict__ kmax) {
   __shared__ float wmax[4];
   const int t = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int r = threadIdx.x >> 2, qd = threadIdx.x & 3;
-  const int n = min(t * kBlockK + r, N - 1);
-  const int dq = D / 4;
-  const __bf16* kp = k + b * sb + h * sh + (int64_t)n * sn + qd * dq;
-  float ss = 0.0f;
-  for (int i = 0; i < dq; i += 8) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(kp + i);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cpr = D / 8;                 // 16-byte chunks per row (16 or 8)
+  const int rpi = 64 / cpr;              // rows per load instruction (4 or 8)
+  const int rpw = kBlockK / 4;           // rows per wave (16)
+  const __bf16* kb = k + b * sb + h * sh;
+  float m = 0.0f;
+  for (int r0 = 0; r0 < rpw; r0 += rpi) {
+    const int n = min(t * kBlockK + wave * rpw + r0 + lane / cpr, N - 1);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(kb + (int64_t)n * sn + (lane % cpr) * 8);
+    float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float f = (float)v[e];
       ss = fmaf(f, f, ss);
     }
+    for (int off = 1; off < cpr; off <<= 1) ss += __shfl_xor(ss, off);
+    m = fmaxf(m, sqrtf(ss));
   }
-  ss += __shfl_xor(ss, 1);
-  ss += __shfl_xor(ss, 2);
-  float m = sqrtf(ss);
-  for (int off = 32; off >= 4; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  for (int off = cpr; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) wmax[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0)
     kmax[(int64_t)bh * nkt + t] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));

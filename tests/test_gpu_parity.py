@@ -119,6 +119,28 @@ def test_temperature_q_k_scaled():
             what="q,k ~ N(0,4)")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_outlier_keys(d):
+    """A few keys are 24x a query row: that row's logit reaches about 400 in
+    log2 units while the rest stay near 10, and every other row sees logits
+    of tens from them. The exact row max must be taken exactly on the tiles
+    that hold those keys, which the per-tile key-norm bound decides; an
+    underestimated bound would skip it and exp2 would overflow. Peaky rows:
+    the element gate is the derived 2^-6 max|V| of the temperature test."""
+    lay = framed_layout()
+    q, k, v = qkv_random(1, 2, lay.n, d, seed=11)
+    rng = np.random.default_rng(11)
+    keys = rng.choice(lay.n, size=6, replace=False)
+    rows = rng.choice(lay.n, size=6, replace=False)
+    for kk, r in zip(keys, rows):
+        k[0, :, kk] = (q[0, :, r].float() * 24.0).to(k.dtype)
+    o, l = run_gpu(q, k, v, lay, DEF)
+    ro, rl = run_oracle(q, k, v, lay, DEF)
+    assert float(rl.max()) > 200.0
+    compare(o.numpy(), l.numpy(), ro, rl, tol_o=2.0 ** -6 * float(v.float().abs().max()),
+            what=f"outlier keys, d={d}")
+
+
 @pytest.mark.parametrize("parts,bounds", [(3, None), (1, None), (4, "segments"), (5, "ragged")])
 def test_partitioned_matches(parts, bounds):
     lay = small_layout(mask=True, pictures=3)
