@@ -98,7 +98,20 @@ def cpu_baseline(cfg, q, k, v, lay, seconds: float):
     flop = oracle.flops(1, 1, lay.n, cfg.head_dim, rows=done)
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} stratified query rows of head 0 of {cfg.name} against all {lay.n} keys, "
-                      f"fp64 NumPy oracle, {dt:.1f} s"}
+                      f"fp64 NumPy oracle, {dt:.1f} s",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
