@@ -39,6 +39,21 @@ def test_fullsize_sampled_rows(cid):
     compare(o.numpy(), l.numpy(), ro, rl, what=f"config {cid} fused sampled")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fullsize_bnhd_sampled_rows(d):
+    """The headline sequence (107,126 tokens) with 8 heads stored [B][N][H][D]
+    (the row stride spans all heads) at head dim 64 and 128: the strided
+    staging path at full length, checked on sampled rows of two heads."""
+    lay = ti.config(6).layout()
+    g = torch.Generator().manual_seed(6100 + d)
+    q, k, v = (torch.randn(1, 8, lay.n, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    rows = sample_rows(lay, n_random=128, per_segment=32, seed=61)
+    log(f"N={lay.n} H=8 D={d} BNHD; comparing {len(rows)} rows x heads [0, 7]")
+    o, l = run_gpu(q, k, v, lay, ti.Params(), layout="bnhd", heads=[0, 7], rows=rows)
+    ro, rl = run_oracle(q, k, v, lay, ti.Params(), rows=rows, heads=[0, 7])
+    compare(o.numpy(), l.numpy(), ro, rl, what=f"BNHD H=8 D={d} sampled")
+
+
 def test_fullsize_binding_partitioned():
     cfg = ti.config(5)
     lay = cfg.layout()
