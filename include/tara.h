@@ -200,9 +200,11 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
  *           contents on entry are ignored, on exit unspecified.
  *  stream   HIP stream the work is enqueued on.
  *
- * Metadata out of range (seg_type > 3, picture id outside [0, num_pictures),
- * non-finite time on a TARGET/GUIDE token) is not an error by default: such a
- * token gets no bias term, never an out-of-bounds read. With the environment
+ * Metadata out of range is not an error by default and never causes an
+ * out-of-bounds read; the token loses only the term its bad field feeds:
+ * seg_type > 3 makes it an OTHER token, a picture id outside [0, num_pictures)
+ * removes its binding term, a non-finite time takes a GUIDE key or a TARGET
+ * query out of the temporal term (the query keeps its binding term). With the environment
  * variable TARA_VALIDATE=1 the metadata is copied to the host and checked
  * first (synchronously), returning TARA_ERR_BAD_METADATA.
  * B, H or N == 0 is a valid empty call and enqueues nothing. */
