@@ -34,6 +34,23 @@ def test_exports_every_declared_symbol(lib):
     assert sorted(tara.EXPORTED_SYMBOLS) == names
 
 
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library every entry point raises; there is no fallback."""
+    import sys
+    code = ("import temporally_biased_flashattention_amd as t\n"
+            "for f in (t.load_library, t.tara_params_default):\n"
+            "    try:\n"
+            "        f()\n"
+            "    except t.TaraLibraryMissing as e:\n"
+            "        print('missing:', f.__name__)\n"
+            "    else:\n"
+            "        raise SystemExit(f.__name__ + ' did not raise')\n")
+    env = dict(os.environ, TARA_LIBRARY=str(tmp_path / "absent.so"), PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.count("missing:") == 2
+
+
 def test_params_struct_matches_header_defaults():
     p = tara.tara_params_default()
     assert (p.window, p.falloff, p.strength, p.cap) == pytest.approx((0.20, 0.25, 2.0, 6.0))
