@@ -42,6 +42,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_headline_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "temporally_biased_flashattention_amd", "csrc", "tara_kernels.hip")
 
 
+def attention_flop(b: int, h: int, rows: int, n: int, d: int) -> float:
+    """Effective work of the dense path: both products over every (query row,
+    key) pair, 2 FLOP per multiply-add, Q.K^T and P.V each rows * n * d
+    multiply-adds per head; bias skipping removes no contraction work."""
+    return 4.0 * b * h * rows * n * d
+
+
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -77,7 +84,7 @@ def cpu_baseline(cfg, q, k, v, lay, seconds: float):
     import numpy as np
 
     import oracle
-    from tests.tara_testlib import sample_rows
+    from tara_inputs import sample_rows
     try:
         from threadpoolctl import threadpool_info
         cores = max([int(i.get("num_threads", 0)) for i in threadpool_info()] + [1])
@@ -95,7 +102,7 @@ def cpu_baseline(cfg, q, k, v, lay, seconds: float):
         oracle.attention_head(qh, kh, vh, lay.seg, lay.time, lay.picture, lay.mask, p, rows=r)
         done += len(r)
     dt = time.perf_counter() - t0
-    flop = oracle.flops(1, 1, lay.n, cfg.head_dim, rows=done)
+    flop = attention_flop(1, 1, done, lay.n, cfg.head_dim)
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} stratified query rows of head 0 of {cfg.name} against all {lay.n} keys, "
                       f"fp64 NumPy oracle, {dt:.1f} s",
@@ -206,7 +213,7 @@ def main():
         log(f"copy calibration: 3 copies of {nb} bytes")
         del src, dst
 
-    flop = 4.0 * B * H * float(N) * N * D
+    flop = attention_flop(B, H, N, N, D)
     ms_step = elapsed / args.steps * 1e3
     value = flop / (ms_step / 1e3) / 1e12
     k_avg = sum(kms) / len(kms) if kms else float("nan")

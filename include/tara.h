@@ -193,8 +193,9 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
  *  picture_id device int16 [B][N], 0-based picture id of PICTURE tokens; read
  *           only when binding is active; may be NULL when it is not.
  *  mask_weight device fp32 [num_bindings][B][N] mask weight m of TARGET
- *           queries, one plane per binding, or NULL for m = 1 everywhere
- *           ("no mask means the whole output video").
+ *           queries, one plane per binding, or NULL for m = 1 on every target
+ *           query ("BFS H3 Reference Attention Binding (Experimental)",
+ *           section "Inputs you'll set"). Read only when binding is active.
  *  p        host, the controls (see tara_params_t).
  *  workspace device, >= tara_workspace_bytes(...) bytes, 256-byte aligned;
  *           contents on entry are ignored, on exit unspecified.
@@ -204,7 +205,8 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
  * out-of-bounds read; the token loses only the term its bad field feeds:
  * seg_type > 3 makes it an OTHER token, a picture id outside [0, num_pictures)
  * removes its binding term, a non-finite time takes a GUIDE key or a TARGET
- * query out of the temporal term (the query keeps its binding term). With the environment
+ * query out of the temporal term (the query keeps its binding term), and a
+ * non-finite mask weight removes that binding's term for its query. With the environment
  * variable TARA_VALIDATE=1 the metadata is copied to the host and checked
  * first (synchronously), returning TARA_ERR_BAD_METADATA.
  * B, H or N == 0 is a valid empty call and enqueues nothing. */
@@ -224,7 +226,22 @@ const char* tara_status_string(int status);
  * stays valid until this thread's next tara_* call. */
 const char* tara_last_error(void);
 
-/* What the last successful tara_attn_fwd on this thread ran. */
+/* What the last successful tara_attn_fwd on this thread ran.
+ *
+ * Tile classes (debug readback). The bf16 kernel applies the bias per key tile
+ * of 64 keys and per wave of 32 query rows: for each row a constant over the
+ * tile (plain: no bias; saturated: a guide tile entirely past the saturation
+ * gap window + falloff*sqrt(cap/strength), every logit -cap; window: a guide
+ * tile entirely inside the free window; picture: a tile of one bound
+ * picture's keys, the row's summed log gain), or the per-element formula when
+ * some row of the wave needs it (elem: mixed tiles, guide tiles straddling a
+ * knot, partition edges, or every tile under TARA_DISABLE_TILE_SKIP=1). With
+ * the environment variable TARA_TILE_STATS=1 (or TARA_LOG=1), a bf16 call in
+ * FUSED or PARTITIONED mode replays that decision for every (query row, key
+ * tile) pair in a debug kernel, waits for the stream and fills the tiles_*
+ * counts, summed over batch elements and heads (so they add up to
+ * B * H * N * the number of key tiles visited); tile_stats is then 1.
+ * Otherwise tile_stats is 0 and the counts are 0. */
 typedef struct {
   int mode;              /* tara_mode_t */
   int dtype;             /* tara_dtype_t */
@@ -234,7 +251,11 @@ typedef struct {
   int block_q;           /* query rows per workgroup of the attention kernel */
   int block_k;           /* keys per tile */
   int grid;              /* workgroups of the attention kernel (all partitions) */
-  int launches;          /* kernels enqueued by the call */
+  int launches;          /* kernels enqueued by the call (the debug kernel not counted) */
+  int elem_all;          /* 1 when TARA_DISABLE_TILE_SKIP=1 sent every tile down the per-element path */
+  int tile_stats;        /* 1 when the counts below were taken */
+  int reserved;
+  long long tiles_plain, tiles_saturated, tiles_window, tiles_picture, tiles_elem;
 } tara_run_info_t;
 
 /* Copies the run info of this thread's last successful call; TARA_ERR_NULL_POINTER

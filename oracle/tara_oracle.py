@@ -335,9 +335,3 @@ def attention_bruteforce(q, k, v, seg, time, picture, mask, params, scale=None):
         out_o.append([math.fsum(w[j] * float(v[j][c]) for j in range(n)) for c in range(d)])
         out_l.append(lse)
     return np.array(out_o), np.array(out_l)
-
-
-def flops(b: int, h: int, n: int, d: int, rows: Optional[int] = None) -> float:
-    """Effective work of the dense path: two products over every (query, key) pair."""
-    r = n if rows is None else rows
-    return 4.0 * b * h * r * n * d

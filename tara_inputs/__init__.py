@@ -285,3 +285,25 @@ def random_layout(rng: np.random.Generator, n: int, frames: int = 5, pictures: i
     if shuffle:
         lay = lay.permuted(rng.permutation(n))
     return lay
+
+
+def sample_rows(lay: Layout, n_random: int = 256, per_segment: int = 64, seed: int = 0, tail: int = 64):
+    """Stratified query rows: first/last token of each target frame, random
+    target rows, random rows from each other segment, and the last rows."""
+    rng = np.random.default_rng(seed)
+    n = lay.n
+    rows = set()
+    tgt = np.nonzero(lay.seg == SEG_TARGET)[0]
+    if tgt.size:
+        fr = lay.frame[tgt]
+        for f in np.unique(fr):
+            idx = tgt[fr == f]
+            rows.add(int(idx[0]))
+            rows.add(int(idx[-1]))
+        rows.update(int(x) for x in rng.choice(tgt, size=min(n_random, tgt.size), replace=False))
+    for s in (SEG_GUIDE, SEG_PICTURE, SEG_OTHER):
+        idx = np.nonzero(lay.seg == s)[0]
+        if idx.size:
+            rows.update(int(x) for x in rng.choice(idx, size=min(per_segment, idx.size), replace=False))
+    rows.update(range(max(0, n - tail), n))
+    return np.array(sorted(rows), dtype=np.int64)

@@ -85,7 +85,9 @@ class TaraParams(ctypes.Structure):
 class TaraRunInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "mode", "dtype", "bias_active", "binding_active", "num_partitions",
-        "block_q", "block_k", "grid", "launches")]
+        "block_q", "block_k", "grid", "launches", "elem_all", "tile_stats", "reserved")] + [
+        (n, ctypes.c_longlong) for n in (
+            "tiles_plain", "tiles_saturated", "tiles_window", "tiles_picture", "tiles_elem")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -206,6 +208,56 @@ def tara_workspace_bytes(dtype: int, B: int, H: int, N: int, D: int, params: Tar
     return int(n)
 
 
+def _check_call_args(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight, params, workspace):
+    """Raises ValueError unless every buffer has the device, dtype, shape and
+    layout tara_attn_fwd reads or writes, so that no kernel is launched on a
+    buffer too small for it. Shapes and dtypes are checked before devices."""
+    import torch
+
+    def need(cond, msg):
+        if not cond:
+            raise ValueError(msg)
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("seg_type", seg_type),
+                    ("token_time", token_time)):
+        need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    need(q.dim() == 4, "q must be 4-D [B, H, N, D] (views allowed)")
+    B, H, N, D = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        need(t.shape == q.shape, f"{name} has shape {tuple(t.shape)}, q has {tuple(q.shape)}")
+        need(t.dtype == q.dtype, f"{name} is {t.dtype}, q is {q.dtype}")
+    need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N) and lse.is_contiguous(),
+         f"lse must be contiguous float32 [{B}, {H}, {N}]")
+    need(seg_type.dtype == torch.uint8 and tuple(seg_type.shape) == (B, N) and seg_type.is_contiguous(),
+         f"seg_type must be contiguous uint8 [{B}, {N}]")
+    need(token_time.dtype == torch.float32 and tuple(token_time.shape) == (B, N) and token_time.is_contiguous(),
+         f"token_time must be contiguous float32 [{B}, {N}]")
+    if picture_id is not None:
+        need(isinstance(picture_id, torch.Tensor) and picture_id.dtype == torch.int16
+             and tuple(picture_id.shape) == (B, N) and picture_id.is_contiguous(),
+             f"picture_id must be contiguous int16 [{B}, {N}] or None")
+    if mask_weight is not None:
+        need(isinstance(mask_weight, torch.Tensor) and mask_weight.dtype == torch.float32
+             and mask_weight.is_contiguous(), "mask_weight must be a contiguous float32 tensor or None")
+        if params.binding_enabled:
+            # planes [J, B, N]; the library reads the first num_bindings of them
+            nb = max(int(params.num_bindings), 1)
+            want = (B, N) if nb == 1 else (nb, B, N)
+            need(mask_weight.dim() >= 2 and tuple(mask_weight.shape[-2:]) == (B, N)
+                 and mask_weight.numel() >= nb * B * N,
+                 f"mask_weight must hold {list(want)} (one [B, N] plane per binding), got {tuple(mask_weight.shape)}")
+    if workspace is not None:
+        need(isinstance(workspace, torch.Tensor) and workspace.is_contiguous(),
+             "workspace must be a contiguous tensor")
+    dev = q.device
+    need(dev.type == "cuda", f"q is on {dev}; tara_attn_fwd needs HIP device tensors")
+    for name, t in (("k", k), ("v", v), ("o", o), ("lse", lse), ("seg_type", seg_type),
+                    ("token_time", token_time), ("picture_id", picture_id), ("mask_weight", mask_weight),
+                    ("workspace", workspace)):
+        if t is not None:
+            need(t.device == dev, f"{name} is on {t.device}, q is on {dev}")
+
+
 def tara_attn_fwd(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight,
                   params: TaraParams, workspace, stream=None) -> None:
     """Calls tara_attn_fwd on torch device tensors.
@@ -216,12 +268,17 @@ def tara_attn_fwd(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight
     binding), [J, B, N] (J chained bindings, contiguous) or None;
     workspace: a byte tensor of at least tara_workspace_bytes(...) bytes.
     stream: a torch.cuda.Stream (default: the current stream).
+    Buffers of the wrong device, dtype, shape or layout raise ValueError
+    before the library is called.
     """
     import torch
+    _check_call_args(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight, params, workspace)
     lib = load_library()
     B, H, N, D = q.shape
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    elif stream.device != q.device:
+        raise ValueError(f"stream is on {stream.device}, q is on {q.device}")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.tara_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), B, H, N, D,

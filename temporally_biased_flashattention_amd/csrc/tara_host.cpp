@@ -36,7 +36,7 @@ bool env_flag(const char* name) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tq, tk, kp, gt, ksum, vt, kmax, k8, ks, dbias, opart, lsepart, total;
+  size_t tq, tk, kp, gt, ksum, vt, kmax, k8, ks, dbias, opart, lsepart, tstats, total;
 };
 
 int npad_of(int N) { return (N + tara::kBlockK - 1) / tara::kBlockK * tara::kBlockK; }
@@ -79,6 +79,8 @@ WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tar
   L.kp = take((size_t)B * npad * 4);
   L.gt = take((size_t)B * N * table_pictures(p) * 4);
   L.ksum = take((size_t)B * nkt * sizeof(tara::KeyTileSummary));
+  // tile-class counts of the debug readback (bf16 FUSED / PARTITIONED)
+  L.tstats = take((size_t)B * tara::tile_stats_groups(N) * tara::TC_COUNT * 4);
   L.vt = dtype == TARA_BF16 ? take((size_t)B * H * D * npad * 2) : 0;
   L.kmax = dtype == TARA_BF16 ? take((size_t)B * H * nkt * 4) : 0;
   if (uses_qk8(dtype, p)) {
@@ -192,6 +194,367 @@ std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
 
 }  // namespace
 
+namespace tara {
+
+int set_error(int status, const std::string& msg) { return fail(status, msg); }
+
+void set_last_info(const tara_run_info_t& info) {
+  g_info = info;
+  g_info_valid = true;
+}
+
+void set_empty_info(const Call& c) {
+  tara_run_info_t info{};
+  info.mode = c.p->mode;
+  info.dtype = (int)c.dtype;
+  info.num_partitions = num_parts(c.p);
+  info.block_k = kBlockK;
+  set_last_info(info);
+}
+
+int make_call(Call& c, const void* q, const void* k, const void* v, void* o, float* lse, tara_dtype_t dtype, int B,
+              int H, int N, int D, const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
+              const int64_t o_str[3], const uint8_t* seg_type, const float* token_time, const int16_t* picture_id,
+              const float* mask_weight, const tara_params_t* p) {
+  if (!p) return fail(TARA_ERR_NULL_POINTER, "params are NULL");
+  if (dtype != TARA_BF16 && dtype != TARA_FP32) return fail(TARA_ERR_UNSUPPORTED_DTYPE, "dtype must be TARA_BF16 or TARA_FP32");
+  if (D != 64 && D != 128) return fail(TARA_ERR_UNSUPPORTED_HEAD_DIM, "head dim must be 64 or 128");
+  if (B < 0 || H < 0 || N < 0) return fail(TARA_ERR_BAD_SHAPE, "B, H and N must be >= 0");
+  if ((int64_t)B * H > 65535) return fail(TARA_ERR_BAD_SHAPE, "B * H must be <= 65535");
+  if (N > (1 << 30)) return fail(TARA_ERR_BAD_SHAPE, "N must be <= 2^30");
+  if (p->mode == TARA_MODE_THREE_TERM && npad_of(N) / kBlockK > kMaxListTiles)
+    return fail(TARA_ERR_BAD_SHAPE, "three-term mode supports N <= 2^20 (its key-tile lists live in LDS)");
+  if (int st = check_params(p, N)) return st;
+  if (!qk8_supported(dtype, p)) return fail(TARA_ERR_BAD_PARAM, "qk8 requires TARA_BF16 and TARA_MODE_FUSED");
+  if (p->mode == TARA_MODE_DENSE_BIAS && dtype != TARA_BF16)
+    return fail(TARA_ERR_BAD_PARAM, "TARA_MODE_DENSE_BIAS requires TARA_BF16");
+  c.p = p;
+  c.dtype = dtype;
+  c.B = B;
+  c.H = H;
+  c.N = N;
+  c.D = D;
+  if (B == 0 || H == 0 || N == 0) return TARA_OK;
+  if (!q || !k || !v || !o || !lse) return fail(TARA_ERR_NULL_POINTER, "q, k, v, o and lse must be non-NULL");
+  if (!seg_type || !token_time) return fail(TARA_ERR_NULL_POINTER, "seg_type and token_time must be non-NULL");
+  const int esize = dtype == TARA_BF16 ? 2 : 4;
+  if (int st = check_strides("q", q, q_str, esize)) return st;
+  if (int st = check_strides("k", k, k_str, esize)) return st;
+  if (int st = check_strides("v", v, v_str, esize)) return st;
+  if (int st = check_strides("o", o, o_str, esize)) return st;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3) != 0) return fail(TARA_ERR_BAD_STRIDE, "lse is not 4-byte aligned");
+  // the bf16 kernel stages key tiles with 32-bit byte offsets from one head's
+  // K rows and from its rows of the key-contiguous V copy: N (padded to whole
+  // tiles) rows of K at its row stride, and D rows of that copy, must each
+  // span less than 2^31 bytes
+  if (dtype == TARA_BF16 && ((int64_t)k_str[2] * 2 * npad_of(N) >= (int64_t(1) << 31) ||
+                             (int64_t)D * npad_of(N) * 2 >= (int64_t(1) << 31)))
+    return fail(TARA_ERR_BAD_STRIDE, "K row stride x N or D x N too large for the bf16 kernel's 32-bit tile offsets");
+  bool binding_active = false;
+  if (p->binding_enabled)
+    for (int j = 0; j < num_bindings(p); ++j)
+      for (int i = 0; i < p->num_pictures; ++i) binding_active |= p->picture_gain[j][i] != 1.0f;
+  if (binding_active && !picture_id)
+    return fail(TARA_ERR_NULL_POINTER, "picture_id must be non-NULL when binding is active");
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.o = o;
+  c.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    c.qs[i] = q_str[i];
+    c.ks[i] = k_str[i];
+    c.vs[i] = v_str[i];
+    c.os[i] = o_str[i];
+  }
+  c.seg = seg_type;
+  c.time = token_time;
+  c.pic = picture_id;
+  c.mask = mask_weight;
+  c.mask_plane = (int64_t)B * N;
+  return TARA_OK;
+}
+
+size_t call_workspace(const Call& c) { return ws_layout_for(c.dtype, c.B, c.H, c.N, c.D, c.p).total; }
+
+Call sub_call(const Call& c, int b, int h0, int hc) {
+  Call s = c;
+  const int esize = c.dtype == TARA_BF16 ? 2 : 4;
+  auto at = [&](const void* base, const int64_t* st) {
+    return static_cast<const void*>(static_cast<const char*>(base) + (b * st[0] + h0 * st[1]) * esize);
+  };
+  s.q = at(c.q, c.qs);
+  s.k = at(c.k, c.ks);
+  s.v = at(c.v, c.vs);
+  s.o = const_cast<void*>(at(c.o, c.os));
+  s.lse = c.lse + ((int64_t)b * c.H + h0) * c.N;
+  s.seg = c.seg + (int64_t)b * c.N;
+  s.time = c.time + (int64_t)b * c.N;
+  s.pic = c.pic ? c.pic + (int64_t)b * c.N : nullptr;
+  s.mask = c.mask ? c.mask + (int64_t)b * c.N : nullptr;   // planes stay c.mask_plane apart
+  s.B = 1;
+  s.H = hc;
+  return s;
+}
+
+int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t stream, tara_run_info_t* out) {
+  const tara_params_t* p = c.p;
+  const tara_dtype_t dtype = c.dtype;
+  const int B = c.B, H = c.H, N = c.N, D = c.D;
+  const void *q = c.q, *k = c.k, *v = c.v;
+  void* o = c.o;
+  float* lse = c.lse;
+  const int64_t *q_str = c.qs, *k_str = c.ks, *v_str = c.vs, *o_str = c.os;
+  const uint8_t* seg_type = c.seg;
+  const float* token_time = c.time;
+  const int16_t* picture_id = c.pic;
+  const float* mask_weight = c.mask;
+  const WsLayout L = ws_layout_for(dtype, B, H, N, D, p);
+
+  // derived constants, in double then rounded once to fp32
+  const double log2e = 1.4426950408889634;
+  const double scale = p->softmax_scale > 0.0f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)D);
+  const bool bias_active = p->strength > 0.0f && p->cap > 0.0f;
+  const int nbind = num_bindings(p);
+  bool binding_active = false;
+  if (p->binding_enabled)
+    for (int j = 0; j < nbind; ++j)
+      for (int i = 0; i < p->num_pictures; ++i) binding_active |= p->picture_gain[j][i] != 1.0f;
+
+  const int parts = num_parts(p);
+  const int npad = npad_of(N), nkt = npad / kBlockK;
+
+  MetaArgs ma{};
+  ma.seg = seg_type;
+  ma.time = token_time;
+  ma.pic = picture_id;
+  ma.mask = mask_weight;
+  ma.mask_plane = c.mask_plane;
+  ma.B = B;
+  ma.N = N;
+  ma.npad = npad;
+  ma.nkt = nkt;
+  ma.bias_active = bias_active;
+  ma.binding_active = binding_active;
+  ma.num_pictures = table_pictures(p);
+  ma.nbind = nbind;
+  for (int j = 0; j < kMaxBindings; ++j)
+    for (int i = 0; i < kMaxPictures; ++i)
+      ma.lg2gain[j][i] = (binding_active && j < nbind && i < p->num_pictures)
+                             ? (float)std::log2((double)p->picture_gain[j][i]) : 0.0f;
+  ma.tq = reinterpret_cast<float*>(ws + L.tq);
+  ma.tk = reinterpret_cast<float*>(ws + L.tk);
+  ma.kp = reinterpret_cast<int*>(ws + L.kp);
+  ma.gt = reinterpret_cast<float*>(ws + L.gt);
+  ma.ksum = reinterpret_cast<KeyTileSummary*>(ws + L.ksum);
+
+  AttnArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.vt = dtype == TARA_BF16 ? reinterpret_cast<const __bf16*>(ws + L.vt) : nullptr;
+  aa.q_sb = q_str[0]; aa.q_sh = q_str[1]; aa.q_sn = q_str[2];
+  aa.k_sb = k_str[0]; aa.k_sh = k_str[1]; aa.k_sn = k_str[2];
+  aa.v_sb = v_str[0]; aa.v_sh = v_str[1]; aa.v_sn = v_str[2];
+  aa.o_sb = o_str[0]; aa.o_sh = o_str[1]; aa.o_sn = o_str[2];
+  aa.o = o;
+  aa.lse = lse;
+  // per-partition outputs: every mode but fused (range partitions, the three terms)
+  aa.opart = has_partials(p) ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
+  aa.lsepart = has_partials(p) ? reinterpret_cast<float*>(ws + L.lsepart) : nullptr;
+  aa.B = B;
+  aa.H = H;
+  aa.N = N;
+  aa.npad = npad;
+  aa.nkt = nkt;
+  aa.tq = ma.tq;
+  aa.tk = ma.tk;
+  aa.kp = ma.kp;
+  aa.gt = ma.gt;
+  aa.npics = ma.num_pictures;
+  aa.ksum = ma.ksum;
+  aa.kmax = dtype == TARA_BF16 ? reinterpret_cast<const float*>(ws + L.kmax) : nullptr;
+  const bool qk8 = uses_qk8(dtype, p);
+  aa.k8 = qk8 ? reinterpret_cast<const uint8_t*>(ws + L.k8) : nullptr;
+  aa.ks = qk8 ? reinterpret_cast<const float*>(ws + L.ks) : nullptr;
+  aa.c = (float)(scale * log2e);
+  const double sigma = bias_active ? std::sqrt((double)p->strength * log2e) / (double)p->falloff : 0.0;
+  aa.sigma = (float)sigma;
+  aa.w = (float)((double)p->window * sigma);
+  aa.cap2 = bias_active ? (float)((double)p->cap * log2e) : 0.0f;
+  aa.window = p->window;
+  aa.dsat = bias_active ? (float)((double)p->window + (double)p->falloff * std::sqrt((double)p->cap / (double)p->strength))
+                        : INFINITY;
+  aa.corr0 = bias_active ? (float)std::log2(-std::expm1(-(double)p->cap)) : -INFINITY;
+  // TARA_DISABLE_TILE_SKIP=1: every key tile takes the per-element bias (the
+  // tile classes are switched off; the results are the same up to rounding)
+  aa.elem_all = env_flag("TARA_DISABLE_TILE_SKIP") ? 1 : 0;
+  aa.nparts = parts;
+  if (p->mode == TARA_MODE_PARTITIONED && p->partition_bounds) {
+    for (int i = 0; i <= parts; ++i) aa.kr[i] = p->partition_bounds[i];
+  } else {
+    for (int i = 0; i <= parts; ++i) aa.kr[i] = (int)((int64_t)N * i / parts);
+  }
+  const bool partitioned = has_partials(p);
+  aa.qr0 = 0;
+  aa.qr1 = N;
+  // query ranges, each its own launch of every pass (FRAME_LOOP: the caller's
+  // ranges; otherwise all rows at once)
+  std::vector<std::pair<int, int>> qranges;
+  if (p->mode == TARA_MODE_FRAME_LOOP) {
+    const int nr = p->num_partitions;
+    for (int i = 0; i < nr; ++i) {
+      const int r0 = p->partition_bounds ? p->partition_bounds[i] : (int)((int64_t)N * i / nr);
+      const int r1 = p->partition_bounds ? p->partition_bounds[i + 1] : (int)((int64_t)N * (i + 1) / nr);
+      if (r1 > r0) qranges.emplace_back(r0, r1);
+    }
+  } else {
+    qranges.emplace_back(0, N);
+  }
+  // passes of the attention kernel: one fused pass, one pass over all key
+  // ranges, or the three terms
+  std::vector<int> passes;
+  if (p->mode == TARA_MODE_PARTITIONED) passes = {PASS_RANGE};
+  else if (p->mode == TARA_MODE_THREE_TERM) passes = {PASS_TERM_A, PASS_TERM_B, PASS_TERM_C};
+  else passes = {PASS_FUSED};
+  const bool dense = p->mode == TARA_MODE_DENSE_BIAS;
+  aa.dbias = dense ? reinterpret_cast<const float*>(ws + L.dbias) : nullptr;
+  const int variant = qk8 ? ATTN_QK8 : dense ? ATTN_DENSE_BIAS : ATTN_PLAIN;
+  int launches = 0;
+  hipError_t e = hipSuccess;
+  if (run_meta) {
+    e = launch_meta(ma, stream);
+    ++launches;
+  }
+  if (e == hipSuccess && dtype == TARA_BF16) {
+    e = launch_vtranspose(static_cast<const __bf16*>(v), v_str[0], v_str[1], v_str[2],
+                                const_cast<__bf16*>(aa.vt), B, H, N, npad, D, stream);
+    ++launches;
+    if (e == hipSuccess) {
+      // key norms per tile; with 8-bit Q.K the same kernel also writes the FP8 keys and tile scales
+      if (qk8)
+        e = launch_kquant(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
+                                const_cast<uint8_t*>(aa.k8), const_cast<float*>(aa.ks), const_cast<float*>(aa.kmax),
+                                B, H, N, npad, nkt, D, stream);
+      else
+        e = launch_knorm(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
+                               const_cast<float*>(aa.kmax), B, H, N, nkt, D, stream);
+      ++launches;
+    }
+  }
+  if (e == hipSuccess && dense) {
+    // the dense-bias baseline: every bias value written out before the attention pass
+    e = launch_dense_bias(aa, const_cast<float*>(aa.dbias), stream);
+    ++launches;
+  }
+  if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
+
+  for (int pass : passes)
+    if (pass != PASS_FUSED && (!aa.opart || !aa.lsepart))
+      return fail(TARA_ERR_HIP, "internal: a partition pass without its partial-output buffers");
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (debug) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timing) {
+      if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) {
+        if (ev0) (void)hipEventDestroy(ev0);
+        return fail(TARA_ERR_HIP, "hipEventCreate failed");
+      }
+      (void)hipEventRecord(ev0, stream);
+    }
+  }
+  int grid = 0, block_q = 0;
+  for (const auto& qrange : qranges) {
+    aa.qr0 = qrange.first;
+    aa.qr1 = qrange.second;
+    for (int pass : passes) {
+      if (dtype == TARA_BF16) {
+        block_q = attn_bf16_block_q(D);
+        aa.nqb = (aa.qr1 - aa.qr0 + block_q - 1) / block_q;
+        grid += attn_bf16_grid(aa) * (pass == PASS_RANGE ? parts : 1);
+        e = launch_attn_bf16(aa, D, pass, variant, stream);
+      } else {
+        block_q = attn_f32_block_q(D);
+        aa.nqb = (aa.qr1 - aa.qr0 + block_q - 1) / block_q;
+        grid += aa.nqb * B * H * (pass == PASS_RANGE ? parts : 1);
+        e = launch_attn_f32(aa, D, pass, stream);
+      }
+      ++launches;
+      if (e != hipSuccess) break;
+    }
+    if (e != hipSuccess) break;
+  }
+  if (ev1) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    (void)hipEventRecord(ev1, stream);
+    g_events.emplace_back(ev0, ev1);
+  }
+  if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
+  if (partitioned) {
+    MergeArgs mg{};
+    mg.opart = aa.opart;
+    mg.lsepart = aa.lsepart;
+    mg.o = o;
+    mg.lse = lse;
+    mg.o_sb = o_str[0]; mg.o_sh = o_str[1]; mg.o_sn = o_str[2];
+    mg.B = B; mg.H = H; mg.N = N; mg.D = D; mg.nparts = parts;
+    e = launch_merge(mg, dtype == TARA_BF16, stream);
+    ++launches;
+    if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  }
+  const int parts_info = p->mode == TARA_MODE_FRAME_LOOP ? (int)qranges.size() : parts;
+  tara_run_info_t info{};
+  info.mode = p->mode;
+  info.dtype = (int)dtype;
+  info.bias_active = bias_active;
+  info.binding_active = binding_active;
+  info.num_partitions = parts_info;
+  info.block_q = block_q;
+  info.block_k = kBlockK;
+  info.grid = grid;
+  info.launches = launches;
+  info.elem_all = aa.elem_all;
+  const bool log = env_flag("TARA_LOG");
+  if (debug && (log || env_flag("TARA_TILE_STATS")) && dtype == TARA_BF16 &&
+      (p->mode == TARA_MODE_FUSED || p->mode == TARA_MODE_PARTITIONED)) {
+    // debug readback: replay the bias-class decisions and count them (synchronous)
+    const int ng = tile_stats_groups(N);
+    unsigned* dcounts = reinterpret_cast<unsigned*>(ws + L.tstats);
+    std::vector<unsigned> hc((size_t)B * ng * TC_COUNT);
+    e = launch_tile_stats(aa, partitioned ? PASS_RANGE : PASS_FUSED, dcounts, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(hc.data(), dcounts, hc.size() * 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("tile statistics: ") + hipGetErrorString(e));
+    long long t[TC_COUNT] = {};
+    for (size_t i = 0; i < hc.size(); ++i) t[i % TC_COUNT] += hc[i];
+    info.tile_stats = 1;
+    info.tiles_plain = t[TC_PLAIN] * H;
+    info.tiles_saturated = t[TC_SATURATED] * H;
+    info.tiles_window = t[TC_WINDOW] * H;
+    info.tiles_picture = t[TC_PICTURE] * H;
+    info.tiles_elem = t[TC_ELEM] * H;
+  }
+  *out = info;
+  if (log && debug) {
+    std::fprintf(stderr, "[tara] %s %s B=%d H=%d N=%d D=%d bias=%d binding=%d parts=%d grid=%d launches=%d%s",
+                 p->mode == TARA_MODE_THREE_TERM   ? "three-term"
+                 : p->mode == TARA_MODE_DENSE_BIAS ? "dense-bias"
+                 : p->mode == TARA_MODE_FRAME_LOOP ? "frame-loop"
+                 : partitioned                     ? "partitioned"
+                                                   : "fused",
+                 dtype == TARA_BF16 ? "bf16" : "fp32", B, H, N, D,
+                 (int)bias_active, (int)binding_active, parts_info, grid, launches,
+                 aa.elem_all ? " tile-skip=off" : "");
+    if (info.tile_stats)
+      std::fprintf(stderr, " tiles plain=%lld saturated=%lld window=%lld picture=%lld elem=%lld",
+                   info.tiles_plain, info.tiles_saturated, info.tiles_window, info.tiles_picture, info.tiles_elem);
+    std::fprintf(stderr, "\n");
+  }
+  return TARA_OK;
+}
+
+}  // namespace tara
+
 extern "C" {
 
 void tara_params_default(tara_params_t* p) {
@@ -280,248 +643,25 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   const tara_params_t* p, void* workspace, size_t workspace_bytes, tara_stream_t stream_) {
   g_err.clear();
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  if (!p) return fail(TARA_ERR_NULL_POINTER, "params are NULL");
-  if (dtype != TARA_BF16 && dtype != TARA_FP32) return fail(TARA_ERR_UNSUPPORTED_DTYPE, "dtype must be TARA_BF16 or TARA_FP32");
-  if (D != 64 && D != 128) return fail(TARA_ERR_UNSUPPORTED_HEAD_DIM, "head dim must be 64 or 128");
-  if (B < 0 || H < 0 || N < 0) return fail(TARA_ERR_BAD_SHAPE, "B, H and N must be >= 0");
-  if ((int64_t)B * H > 65535) return fail(TARA_ERR_BAD_SHAPE, "B * H must be <= 65535");
-  if (N > (1 << 30)) return fail(TARA_ERR_BAD_SHAPE, "N must be <= 2^30");
-  if (p && p->mode == TARA_MODE_THREE_TERM && npad_of(N) / tara::kBlockK > tara::kMaxListTiles)
-    return fail(TARA_ERR_BAD_SHAPE, "three-term mode supports N <= 2^20 (its key-tile lists live in LDS)");
-  if (int st = check_params(p, N)) return st;
-  if (!qk8_supported(dtype, p)) return fail(TARA_ERR_BAD_PARAM, "qk8 requires TARA_BF16 and TARA_MODE_FUSED");
-  if (p->mode == TARA_MODE_DENSE_BIAS && dtype != TARA_BF16)
-    return fail(TARA_ERR_BAD_PARAM, "TARA_MODE_DENSE_BIAS requires TARA_BF16");
+  tara::Call c{};
+  if (int st = tara::make_call(c, q, k, v, o, lse, dtype, B, H, N, D, q_str, k_str, v_str, o_str, seg_type,
+                               token_time, picture_id, mask_weight, p))
+    return st;
   if (B == 0 || H == 0 || N == 0) {
-    g_info = tara_run_info_t{p->mode, (int)dtype, 0, 0, num_parts(p), 0, tara::kBlockK, 0, 0};
-    g_info_valid = true;
+    tara::set_empty_info(c);
     return TARA_OK;
   }
-  if (!q || !k || !v || !o || !lse) return fail(TARA_ERR_NULL_POINTER, "q, k, v, o and lse must be non-NULL");
-  if (!seg_type || !token_time) return fail(TARA_ERR_NULL_POINTER, "seg_type and token_time must be non-NULL");
-  const int esize = dtype == TARA_BF16 ? 2 : 4;
-  if (int st = check_strides("q", q, q_str, esize)) return st;
-  if (int st = check_strides("k", k, k_str, esize)) return st;
-  if (int st = check_strides("v", v, v_str, esize)) return st;
-  if (int st = check_strides("o", o, o_str, esize)) return st;
-  if ((reinterpret_cast<uintptr_t>(lse) & 3) != 0) return fail(TARA_ERR_BAD_STRIDE, "lse is not 4-byte aligned");
-  // the bf16 kernel stages key tiles with 32-bit byte offsets from one head's
-  // K rows and from its rows of the key-contiguous V copy: N (padded to whole
-  // tiles) rows of K at its row stride, and D rows of that copy, must each
-  // span less than 2^31 bytes
-  if (dtype == TARA_BF16 && ((int64_t)k_str[2] * 2 * npad_of(N) >= (int64_t(1) << 31) ||
-                             (int64_t)D * npad_of(N) * 2 >= (int64_t(1) << 31)))
-    return fail(TARA_ERR_BAD_STRIDE, "K row stride x N or D x N too large for the bf16 kernel's 32-bit tile offsets");
-
-  // derived constants, in double then rounded once to fp32
-  const double log2e = 1.4426950408889634;
-  const double scale = p->softmax_scale > 0.0f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)D);
-  const bool bias_active = p->strength > 0.0f && p->cap > 0.0f;
-  const int nbind = num_bindings(p);
-  bool binding_active = false;
-  if (p->binding_enabled)
-    for (int j = 0; j < nbind; ++j)
-      for (int i = 0; i < p->num_pictures; ++i) binding_active |= p->picture_gain[j][i] != 1.0f;
-  if (binding_active && !picture_id)
-    return fail(TARA_ERR_NULL_POINTER, "picture_id must be non-NULL when binding is active");
-
-  const int parts = num_parts(p);
-  const WsLayout L = ws_layout_for(dtype, B, H, N, D, p);
+  const size_t need = tara::call_workspace(c);
   if (!workspace) return fail(TARA_ERR_WORKSPACE, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return fail(TARA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(TARA_ERR_WORKSPACE, "workspace needs " + std::to_string(L.total) + " bytes, got " +
+  if (workspace_bytes < need)
+    return fail(TARA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
                                         std::to_string(workspace_bytes));
   if (env_flag("TARA_VALIDATE"))
     if (int st = validate_metadata(B, N, seg_type, token_time, picture_id, mask_weight, p, stream)) return st;
-
-  char* ws = static_cast<char*>(workspace);
-  const int npad = npad_of(N), nkt = npad / tara::kBlockK;
-
-  tara::MetaArgs ma{};
-  ma.seg = seg_type;
-  ma.time = token_time;
-  ma.pic = picture_id;
-  ma.mask = mask_weight;
-  ma.B = B;
-  ma.N = N;
-  ma.npad = npad;
-  ma.nkt = nkt;
-  ma.bias_active = bias_active;
-  ma.binding_active = binding_active;
-  ma.num_pictures = table_pictures(p);
-  ma.nbind = nbind;
-  for (int j = 0; j < tara::kMaxBindings; ++j)
-    for (int i = 0; i < tara::kMaxPictures; ++i)
-      ma.lg2gain[j][i] = (binding_active && j < nbind && i < p->num_pictures)
-                             ? (float)std::log2((double)p->picture_gain[j][i]) : 0.0f;
-  ma.tq = reinterpret_cast<float*>(ws + L.tq);
-  ma.tk = reinterpret_cast<float*>(ws + L.tk);
-  ma.kp = reinterpret_cast<int*>(ws + L.kp);
-  ma.gt = reinterpret_cast<float*>(ws + L.gt);
-  ma.ksum = reinterpret_cast<tara::KeyTileSummary*>(ws + L.ksum);
-
-  tara::AttnArgs aa{};
-  aa.q = q;
-  aa.k = k;
-  aa.v = v;
-  aa.vt = dtype == TARA_BF16 ? reinterpret_cast<const __bf16*>(ws + L.vt) : nullptr;
-  aa.q_sb = q_str[0]; aa.q_sh = q_str[1]; aa.q_sn = q_str[2];
-  aa.k_sb = k_str[0]; aa.k_sh = k_str[1]; aa.k_sn = k_str[2];
-  aa.v_sb = v_str[0]; aa.v_sh = v_str[1]; aa.v_sn = v_str[2];
-  aa.o_sb = o_str[0]; aa.o_sh = o_str[1]; aa.o_sn = o_str[2];
-  aa.o = o;
-  aa.lse = lse;
-  // per-partition outputs: every mode but fused (range partitions, the three terms)
-  aa.opart = has_partials(p) ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
-  aa.lsepart = has_partials(p) ? reinterpret_cast<float*>(ws + L.lsepart) : nullptr;
-  aa.B = B;
-  aa.H = H;
-  aa.N = N;
-  aa.npad = npad;
-  aa.nkt = nkt;
-  aa.tq = ma.tq;
-  aa.tk = ma.tk;
-  aa.kp = ma.kp;
-  aa.gt = ma.gt;
-  aa.npics = ma.num_pictures;
-  aa.ksum = ma.ksum;
-  aa.kmax = dtype == TARA_BF16 ? reinterpret_cast<const float*>(ws + L.kmax) : nullptr;
-  const bool qk8 = uses_qk8(dtype, p);
-  aa.k8 = qk8 ? reinterpret_cast<const uint8_t*>(ws + L.k8) : nullptr;
-  aa.ks = qk8 ? reinterpret_cast<const float*>(ws + L.ks) : nullptr;
-  aa.c = (float)(scale * log2e);
-  const double sigma = bias_active ? std::sqrt((double)p->strength * log2e) / (double)p->falloff : 0.0;
-  aa.sigma = (float)sigma;
-  aa.w = (float)((double)p->window * sigma);
-  aa.cap2 = bias_active ? (float)((double)p->cap * log2e) : 0.0f;
-  aa.window = p->window;
-  aa.dsat = bias_active ? (float)((double)p->window + (double)p->falloff * std::sqrt((double)p->cap / (double)p->strength))
-                        : INFINITY;
-  aa.corr0 = bias_active ? (float)std::log2(-std::expm1(-(double)p->cap)) : -INFINITY;
-  aa.nparts = parts;
-  if (p->mode == TARA_MODE_PARTITIONED && p->partition_bounds) {
-    for (int i = 0; i <= parts; ++i) aa.kr[i] = p->partition_bounds[i];
-  } else {
-    for (int i = 0; i <= parts; ++i) aa.kr[i] = (int)((int64_t)N * i / parts);
-  }
-  const bool partitioned = has_partials(p);
-  aa.qr0 = 0;
-  aa.qr1 = N;
-  // query ranges, each its own launch of every pass (FRAME_LOOP: the caller's
-  // ranges; otherwise all rows at once)
-  std::vector<std::pair<int, int>> qranges;
-  if (p->mode == TARA_MODE_FRAME_LOOP) {
-    const int nr = p->num_partitions;
-    for (int i = 0; i < nr; ++i) {
-      const int r0 = p->partition_bounds ? p->partition_bounds[i] : (int)((int64_t)N * i / nr);
-      const int r1 = p->partition_bounds ? p->partition_bounds[i + 1] : (int)((int64_t)N * (i + 1) / nr);
-      if (r1 > r0) qranges.emplace_back(r0, r1);
-    }
-  } else {
-    qranges.emplace_back(0, N);
-  }
-  // passes of the attention kernel: one fused pass, one pass over all key
-  // ranges, or the three terms
-  std::vector<int> passes;
-  if (p->mode == TARA_MODE_PARTITIONED) passes = {tara::PASS_RANGE};
-  else if (p->mode == TARA_MODE_THREE_TERM) passes = {tara::PASS_TERM_A, tara::PASS_TERM_B, tara::PASS_TERM_C};
-  else passes = {tara::PASS_FUSED};
-  const bool dense = p->mode == TARA_MODE_DENSE_BIAS;
-  aa.dbias = dense ? reinterpret_cast<const float*>(ws + L.dbias) : nullptr;
-  const int variant = qk8 ? tara::ATTN_QK8 : dense ? tara::ATTN_DENSE_BIAS : tara::ATTN_PLAIN;
-  int launches = 0;
-  hipError_t e = tara::launch_meta(ma, stream);
-  ++launches;
-  if (e == hipSuccess && dtype == TARA_BF16) {
-    e = tara::launch_vtranspose(static_cast<const __bf16*>(v), v_str[0], v_str[1], v_str[2],
-                                const_cast<__bf16*>(aa.vt), B, H, N, npad, D, stream);
-    ++launches;
-    if (e == hipSuccess) {
-      // key norms per tile; with 8-bit Q.K the same kernel also writes the FP8 keys and tile scales
-      if (qk8)
-        e = tara::launch_kquant(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
-                                const_cast<uint8_t*>(aa.k8), const_cast<float*>(aa.ks), const_cast<float*>(aa.kmax),
-                                B, H, N, npad, nkt, D, stream);
-      else
-        e = tara::launch_knorm(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
-                               const_cast<float*>(aa.kmax), B, H, N, nkt, D, stream);
-      ++launches;
-    }
-  }
-  if (e == hipSuccess && dense) {
-    // the dense-bias baseline: every bias value written out before the attention pass
-    e = tara::launch_dense_bias(aa, const_cast<float*>(aa.dbias), stream);
-    ++launches;
-  }
-  if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
-
-  for (int pass : passes)
-    if (pass != tara::PASS_FUSED && (!aa.opart || !aa.lsepart))
-      return fail(TARA_ERR_HIP, "internal: a partition pass without its partial-output buffers");
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    if (g_timing) {
-      if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess) {
-        if (ev0) (void)hipEventDestroy(ev0);
-        return fail(TARA_ERR_HIP, "hipEventCreate failed");
-      }
-      (void)hipEventRecord(ev0, stream);
-    }
-  }
-  int grid = 0, block_q = 0;
-  for (const auto& qrange : qranges) {
-    aa.qr0 = qrange.first;
-    aa.qr1 = qrange.second;
-    for (int pass : passes) {
-      if (dtype == TARA_BF16) {
-        block_q = tara::attn_bf16_block_q(D);
-        aa.nqb = (aa.qr1 - aa.qr0 + block_q - 1) / block_q;
-        grid += tara::attn_bf16_grid(aa) * (pass == tara::PASS_RANGE ? parts : 1);
-        e = tara::launch_attn_bf16(aa, D, pass, variant, stream);
-      } else {
-        block_q = tara::attn_f32_block_q(D);
-        aa.nqb = (aa.qr1 - aa.qr0 + block_q - 1) / block_q;
-        grid += aa.nqb * B * H * (pass == tara::PASS_RANGE ? parts : 1);
-        e = tara::launch_attn_f32(aa, D, pass, stream);
-      }
-      ++launches;
-      if (e != hipSuccess) break;
-    }
-    if (e != hipSuccess) break;
-  }
-  if (ev1) {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    (void)hipEventRecord(ev1, stream);
-    g_events.emplace_back(ev0, ev1);
-  }
-  if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
-  if (partitioned) {
-    tara::MergeArgs mg{};
-    mg.opart = aa.opart;
-    mg.lsepart = aa.lsepart;
-    mg.o = o;
-    mg.lse = lse;
-    mg.o_sb = o_str[0]; mg.o_sh = o_str[1]; mg.o_sn = o_str[2];
-    mg.B = B; mg.H = H; mg.N = N; mg.D = D; mg.nparts = parts;
-    e = tara::launch_merge(mg, dtype == TARA_BF16, stream);
-    ++launches;
-    if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
-  }
-  const int parts_info = p->mode == TARA_MODE_FRAME_LOOP ? (int)qranges.size() : parts;
-  g_info = tara_run_info_t{p->mode, (int)dtype, bias_active, binding_active, parts_info, block_q, tara::kBlockK,
-                           grid, launches};
-  g_info_valid = true;
-  if (env_flag("TARA_LOG"))
-    std::fprintf(stderr, "[tara] %s %s B=%d H=%d N=%d D=%d bias=%d binding=%d parts=%d grid=%d launches=%d\n",
-                 p->mode == TARA_MODE_THREE_TERM   ? "three-term"
-                 : p->mode == TARA_MODE_DENSE_BIAS ? "dense-bias"
-                 : p->mode == TARA_MODE_FRAME_LOOP ? "frame-loop"
-                 : partitioned                     ? "partitioned"
-                                                   : "fused",
-                 dtype == TARA_BF16 ? "bf16" : "fp32", B, H, N, D,
-                 (int)bias_active, (int)binding_active, parts_info, grid, launches);
+  tara_run_info_t info{};
+  if (int st = tara::enqueue_call(c, static_cast<char*>(workspace), true, true, stream, &info)) return st;
+  tara::set_last_info(info);
   return TARA_OK;
 }
 

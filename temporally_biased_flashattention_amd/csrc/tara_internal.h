@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "tara.h"
+
 namespace tara {
 
 constexpr int kBlockK = 64;          // keys per key tile (all paths)
@@ -63,7 +67,8 @@ struct MetaArgs {
   const uint8_t* seg;
   const float* time;
   const int16_t* pic;
-  const float* mask;       // [nbind][B][N] or NULL
+  const float* mask;       // [nbind][...][N] or NULL; planes mask_plane elements apart
+  int64_t mask_plane;
   int B, N, npad, nkt;
   int bias_active, binding_active, num_pictures, nbind;
   float lg2gain[kMaxBindings][kMaxPictures];
@@ -106,6 +111,7 @@ struct AttnArgs {
   float window;            // seconds: gaps <= window carry no penalty
   float dsat;              // seconds: gaps >= window + falloff*sqrt(cap/strength) carry exactly cap
   float corr0;             // log2(1 - 2^-cap2): term C's logit offset for gaps inside the window
+  int elem_all;            // nonzero: every key tile takes the per-element bias (no tile classes)
   int nparts;
   int kr[kMaxParts + 1];   // partition key offsets (fused: {0, N})
 };
@@ -134,5 +140,50 @@ hipError_t launch_dense_bias(const AttnArgs& a, float* out, hipStream_t s);
 int attn_f32_block_q(int D);
 hipError_t launch_attn_f32(const AttnArgs& a, int D, int pass, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16_out, hipStream_t s);
+
+// Tile-class counts (debug readback, FUSED and RANGE passes): (row, key tile)
+// pairs per bias class, per batch element and group of 32 query rows.
+enum : int { TC_PLAIN = 0, TC_SATURATED = 1, TC_WINDOW = 2, TC_PICTURE = 3, TC_ELEM = 4, TC_COUNT = 5 };
+inline int tile_stats_groups(int N) { return (N + 31) / 32; }
+hipError_t launch_tile_stats(const AttnArgs& a, int pass, unsigned* counts, hipStream_t s);
+
+// ----------------------------------------------------------- host side
+// One tara_attn_fwd call, its arguments checked by make_call. Metadata rows
+// of consecutive batch elements are N apart; mask planes mask_plane apart.
+struct Call {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  tara_dtype_t dtype;
+  int B, H, N, D;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  const uint8_t* seg;
+  const float* time;
+  const int16_t* pic;
+  const float* mask;
+  int64_t mask_plane;
+  const tara_params_t* p;
+};
+// Checks the arguments of tara_attn_fwd (everything but the workspace) and
+// fills c; a nonzero status (with the thread's last error set) on failure.
+int make_call(Call& c, const void* q, const void* k, const void* v, void* o, float* lse, tara_dtype_t dtype, int B,
+              int H, int N, int D, const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
+              const int64_t o_str[3], const uint8_t* seg_type, const float* token_time, const int16_t* picture_id,
+              const float* mask_weight, const tara_params_t* p);
+// Workspace bytes of the call's shape.
+size_t call_workspace(const Call& c);
+// Batch element b, heads [h0, h0 + hc) of c, as a call of its own (B = 1).
+Call sub_call(const Call& c, int b, int h0, int hc);
+// Enqueues the call on stream with a workspace of call_workspace(c) bytes
+// (256-byte aligned). run_meta = false reuses the metadata encodings the
+// workspace already holds for the same batch element. debug: record the
+// timing events and honour TARA_TILE_STATS / TARA_LOG (the tile readback
+// synchronises the stream). Fills *info.
+int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t stream, tara_run_info_t* info);
+void set_last_info(const tara_run_info_t& info);
+void set_empty_info(const Call& c);
+int set_error(int status, const std::string& msg);
 
 }  // namespace tara

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64) void meta_kernel(MetaArgs a) {
   const int n = blockIdx.x * kBlockK + threadIdx.x;
   const bool valid = n < a.N;
   const int64_t mi = (int64_t)b * a.N + n;
-  const int64_t plane = (int64_t)a.B * a.N;   // mask plane stride
+  const int64_t plane = a.mask_plane;   // mask plane stride
   int seg = valid ? (int)a.seg[mi] : 3;
   const float t = valid ? a.time[mi] : 0.0f;
   const bool tfinite = valid && isfinite(t);
@@ -103,10 +103,13 @@ __global__ __launch_bounds__(64) void meta_kernel(MetaArgs a) {
     const bool bq = tgt && a.binding_active;
     // summed log2 gains of this query for every picture: sum_j m_j * log2 gain_j,p
     if (a.num_pictures > 0) {
+      // a non-finite mask weight drops that binding's term for this query
       float m[kMaxBindings];
 #pragma unroll
-      for (int j = 0; j < kMaxBindings; ++j)
+      for (int j = 0; j < kMaxBindings; ++j) {
         m[j] = (bq && j < a.nbind) ? (a.mask ? a.mask[j * plane + mi] : 1.0f) : 0.0f;
+        if (!isfinite(m[j])) m[j] = 0.0f;
+      }
       float* g = a.gt + mi * a.num_pictures;
       for (int p = 0; p < a.num_pictures; ++p) {
         float acc = 0.0f;
@@ -806,7 +809,7 @@ void attn_bf16_kernel(AttnArgs a) {
       __syncthreads();
       base += tot;
     }
-    ntiles = base;
+    ntiles = __builtin_amdgcn_readfirstlane(base);   // the same for every wave
     if (ntiles == 0) {
       write_empty();
       return;
@@ -933,7 +936,7 @@ void attn_bf16_kernel(AttnArgs a) {
       qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
     }
     const int kbase = tile0 * kBlockK;
-    const bool partial = kbase < k0 || kbase + kBlockK > k1;
+    const bool partial = a.elem_all || kbase < k0 || kbase + kBlockK > k1;
     const KeyTileSummary sm0 = load_summary(ks_c, tile0);
     const float gpic0 = gtq[max(sm0.pic, 0)];
     float brow;
@@ -1007,7 +1010,7 @@ void attn_bf16_kernel(AttnArgs a) {
     if (DB && has1) load_dbias(bv1, tw1 * kBlockK);
     stage_k(tw3, s0);
     const int kbase1 = tw1 * kBlockK;
-    const bool partial1 = kbase1 < k0 || kbase1 + kBlockK > k1;
+    const bool partial1 = a.elem_all || kbase1 < k0 || kbase1 + kBlockK > k1;
     // bias class of tile t+1, worked out before phase A (it needs only the
     // tile summary, the row and m, all known here): a per-row constant brow,
     // or the per-element path if some lane needs it (cls_elem); cls_bound:
@@ -1218,6 +1221,58 @@ void attn_bf16_kernel(AttnArgs a) {
 
 #undef KBUF
 #undef VBUF
+
+// ------------------------------------------------------ tile-class counts
+// Debug readback of the bias classes the fused / range pass takes: one wave per
+// group of 32 query rows (the rows one wave of attn_bf16_kernel holds; lanes
+// l and l + 32 hold the same row there, and here). For every key tile of every
+// partition it makes the kernel's decision with the same tile_class_lane, and
+// counts (row, key tile) pairs per class into counts[b][group][TC_*]: the
+// per-element path when some row of the group needs it, else each row's
+// constant class. Rows past N are not counted.
+__global__ __launch_bounds__(64) void tile_stats_kernel(AttnArgs a, int pass, unsigned* __restrict__ counts) {
+  const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x & 31;
+  const int ngroups = gridDim.x;
+  const int row = g * 32 + lane;
+  const bool valid = row < a.N;
+  const int qr = valid ? row : a.N - 1;
+  const float tq = a.tq[(int64_t)b * a.N + qr];
+  const bool qbiased = tq == tq;
+  const float* gtq = a.gt + ((int64_t)b * a.N + qr) * a.npics;
+  unsigned c[TC_COUNT] = {};
+  for (int p = 0; p < a.nparts; ++p) {
+    const int k0 = a.kr[p], k1 = a.kr[p + 1];
+    if (k1 <= k0) continue;
+    for (int kt = k0 / kBlockK; kt < (k1 + kBlockK - 1) / kBlockK; ++kt) {
+      const KeyTileSummary sm = a.ksum[(int64_t)b * a.nkt + kt];
+      const int kbase = kt * kBlockK;
+      const bool partial = a.elem_all || kbase < k0 || kbase + kBlockK > k1;
+      const float gpic = a.npics > 0 ? gtq[max(sm.pic, 0)] : 0.0f;
+      float brow;
+      const bool lane_elem = pass == PASS_RANGE ? tile_class_lane<PASS_RANGE>(sm, partial, qbiased, tq, gpic, a, &brow)
+                                                : tile_class_lane<PASS_FUSED>(sm, partial, qbiased, tq, gpic, a, &brow);
+      int cls;
+      if (wave_any(lane_elem)) cls = TC_ELEM;
+      else if ((sm.kind & KT_CLASS) == KT_PICTURE) cls = TC_PICTURE;
+      else if ((sm.kind & KT_CLASS) == KT_GUIDE && qbiased) cls = brow != 0.0f ? TC_SATURATED : TC_WINDOW;
+      else cls = TC_PLAIN;
+      if (valid) ++c[cls];
+    }
+  }
+  // sum over the group's 32 rows (lanes 32..63 repeat lanes 0..31)
+#pragma unroll
+  for (int i = 0; i < TC_COUNT; ++i) {
+    unsigned x = c[i];
+    for (int off = 16; off >= 1; off >>= 1) x += __shfl_xor(x, off, 32);
+    if (threadIdx.x == 0) counts[((int64_t)b * ngroups + g) * TC_COUNT + i] = x;
+  }
+}
+
+hipError_t launch_tile_stats(const AttnArgs& a, int pass, unsigned* counts, hipStream_t s) {
+  dim3 grid(tile_stats_groups(a.N), a.B);
+  hipLaunchKernelGGL(tile_stats_kernel, grid, dim3(64), 0, s, a, pass, counts);
+  return hipGetLastError();
+}
 
 // Workgroup shape of the bf16 kernel: kWaves waves of 32 query rows.
 constexpr int kWaves = 8;

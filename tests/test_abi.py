@@ -64,6 +64,21 @@ def test_params_struct_matches_header_defaults():
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs a C compiler")
+def test_run_info_layout_matches_c(tmp_path):
+    """The ctypes mirror of tara_run_info_t has the C compiler's size and offsets."""
+    fields = [n for n, _ in tara.TaraRunInfo._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"tara.h\"\nint main(void) {\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(tara_run_info_t, {n}));\n' for n in fields)
+                   + '  printf("%zu\\n", sizeof(tara_run_info_t));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(tara.TaraRunInfo, n).offset for n in fields] + [ctypes.sizeof(tara.TaraRunInfo)]
+    assert got == want
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs a C compiler")
 def test_params_layout_matches_c(tmp_path):
     """The ctypes mirror of tara_params_t has the C compiler's size and offsets."""
     fields = [n for n, _ in tara.TaraParams._fields_]
@@ -87,7 +102,8 @@ def test_workspace_bytes():
     B, H, N, D = 1, 2, 1000, 128
     npad = 1024
     nkt = npad // 64
-    meta = _al(B * N * 4) + 2 * _al(B * npad * 4) + _al(0) + _al(B * nkt * 16)
+    ngroups = (N + 31) // 32     # tile-class counts: 5 per group of 32 query rows
+    meta = _al(B * N * 4) + 2 * _al(B * npad * 4) + _al(0) + _al(B * nkt * 16) + _al(B * ngroups * 5 * 4)
     bf16_extra = _al(B * H * D * npad * 2) + _al(B * H * nkt * 4)     # V^T, per-tile max |k|
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p) == meta + bf16_extra
     assert tara.tara_workspace_bytes(tara.TARA_FP32, B, H, N, D, p) == meta

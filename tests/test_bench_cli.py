@@ -33,3 +33,17 @@ def test_needs_a_gpu_here():
         pytest.skip("a GPU is present")
     r = _run("--steps", "1", "--warmup", "0")
     assert r.returncode == 2 and "needs a GPU" in r.stderr
+
+
+def test_attention_flop_hand_count():
+    """The metric's FLOP count against a count done by hand. One head, 2 query
+    rows, 3 keys, head dim 4: Q.K^T is 2 x 3 dot products of length 4, each 4
+    multiplies and 4 adds = 8 FLOP, 48 in all; P.V is 2 rows x 4 dims, each a
+    sum over 3 keys of 3 multiplies and 3 adds = 6 FLOP, 48 in all; total 96.
+    Batches and heads multiply it: B = 2, H = 3 gives 576."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.attention_flop(1, 1, 2, 3, 4) == 96.0
+    assert bench.attention_flop(2, 3, 2, 3, 4) == 576.0
+    # the headline: 4 * 56 * 107,126^2 * 128
+    assert bench.attention_flop(1, 56, 107126, 107126, 128) == 329039295004672.0

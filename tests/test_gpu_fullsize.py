@@ -1,9 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (all heads, one fused call; partitioned for the binding
-workload too), checked on stratified samples of query rows of three heads
-against the fp64 oracle. Full-scale Q = 0 probes make the attention weights a
-function of the bias alone, so per-segment attention mass checks the temporal
-and binding terms at full size with a tight gate.
+workload too), against the fp64 oracle: stratified samples of query rows on
+three heads, 64 stratified rows on every head, and one head of the benchmark
+workload on all 107,126 rows. The outputs are NaN-poisoned before each call
+and every element of them must be written. Full-scale Q = 0 probes make the
+attention weights a function of the bias alone, so per-segment attention mass
+checks the temporal and binding terms at full size with a tight gate.
 """
 import numpy as np
 import pytest
@@ -25,18 +27,68 @@ def _heads(h):
     return sorted({0, h // 2, h - 1})
 
 
+def _head_rows(lay, seed, count=64):
+    """count stratified query rows: random target rows, 6 rows of each other
+    segment present, and the last 2 rows (the ragged last key tile's rows)."""
+    rng = np.random.default_rng(seed)
+    rows = {lay.n - 2, lay.n - 1}
+    for s in (ti.SEG_GUIDE, ti.SEG_PICTURE, ti.SEG_OTHER):
+        idx = np.nonzero(lay.seg == s)[0]
+        if idx.size:
+            rows.update(int(x) for x in rng.choice(idx, size=min(6, idx.size), replace=False))
+    tgt = np.nonzero(lay.seg == ti.SEG_TARGET)[0]
+    rows.update(int(x) for x in rng.choice(tgt, size=count - len(rows), replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
 @pytest.mark.parametrize("cid", [2, 3, 4, 5, 6])
 def test_fullsize_sampled_rows(cid):
+    """One fused call over all heads; about 730 stratified rows of three heads
+    and 64 stratified rows of every head against the oracle."""
     cfg = ti.config(cid)
     lay = cfg.layout()
     log(f"config {cid} {cfg.name}: N={lay.n} H={cfg.heads}; generating inputs")
     q, k, v = ti.qkv(cfg)
     heads = _heads(cfg.heads)
-    rows = sample_rows(lay, n_random=256, per_segment=64, seed=cid)
-    log(f"running GPU (all {cfg.heads} heads), comparing {len(rows)} rows x heads {heads}")
-    o, l = run_gpu(q, k, v, lay, cfg.params, heads=heads, rows=rows)
-    ro, rl = run_oracle(q, k, v, lay, cfg.params, rows=rows, heads=heads)
-    compare(o.numpy(), l.numpy(), ro, rl, what=f"config {cid} fused sampled")
+    deep = sample_rows(lay, n_random=256, per_segment=64, seed=cid)
+    per_head = [_head_rows(lay, seed=1000 * cid + h) for h in range(cfg.heads)]
+    union = np.unique(np.concatenate([deep] + per_head))
+    at = {int(r): i for i, r in enumerate(union)}
+    log(f"running GPU (all {cfg.heads} heads, poisoned outputs), comparing {len(deep)} rows x heads {heads} "
+        f"and 64 rows on each of the {cfg.heads} heads")
+    o, l = run_gpu(q, k, v, lay, cfg.params, rows=union, poison=True)
+    di = [at[int(r)] for r in deep]
+    ro, rl = run_oracle(q, k, v, lay, cfg.params, rows=deep, heads=heads)
+    compare(o.numpy()[:, heads][:, :, di], l.numpy()[:, heads][:, :, di], ro, rl, what=f"config {cid} fused sampled")
+    go, gl, ref_o, ref_l = [], [], [], []
+    for h, rows in enumerate(per_head):
+        ri = [at[int(r)] for r in rows]
+        ho, hl = run_oracle(q, k, v, lay, cfg.params, rows=rows, heads=[h])
+        go.append(o.numpy()[:, h:h + 1][:, :, ri])
+        gl.append(l.numpy()[:, h:h + 1][:, :, ri])
+        ref_o.append(ho)
+        ref_l.append(hl)
+    compare(np.concatenate(go, 1), np.concatenate(gl, 1), np.concatenate(ref_o, 1), np.concatenate(ref_l, 1),
+            what=f"config {cid} fused, 64 rows on every one of {cfg.heads} heads")
+
+
+def test_fullsize_all_rows_one_head():
+    """The benchmark workload (107,126 tokens x 56 heads, d128) in one fused
+    call with poisoned outputs; head 27 compared with the oracle on all
+    107,126 rows (about 6e12 fp64 FLOP on the host)."""
+    cfg = ti.config(6)
+    lay = cfg.layout()
+    q, k, v = ti.qkv(cfg)
+    h = 27
+    o, l = run_gpu(q, k, v, lay, cfg.params, heads=[h], poison=True)
+    blk = 8192
+    ro = np.zeros((1, 1, lay.n, cfg.head_dim))
+    rl = np.zeros((1, 1, lay.n))
+    for r0 in range(0, lay.n, blk):
+        rows = np.arange(r0, min(r0 + blk, lay.n))
+        ro[:, :, rows], rl[:, :, rows] = run_oracle(q, k, v, lay, cfg.params, rows=rows, heads=[h])
+        log(f"oracle head {h}: rows {r0}..{rows[-1]} done")
+    compare(o.numpy(), l.numpy(), ro, rl, what=f"config 6 head {h}, all {lay.n} rows")
 
 
 @pytest.mark.parametrize("d", [64, 128])

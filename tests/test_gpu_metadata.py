@@ -1,9 +1,10 @@
 """Out-of-range metadata, through the C ABI. By default such a token still
 takes part in attention, nothing is read out of bounds, and it loses only the
 term its bad field feeds: a segment code > 3 makes it an other token, a
-picture id outside [0, num_pictures) removes its binding term, and a
-non-finite time takes a guide key out of the temporal term and a target query
-out of the temporal term (the query keeps its binding term). The result must
+picture id outside [0, num_pictures) removes its binding term, a non-finite
+time takes a guide key out of the temporal term and a target query out of the
+temporal term (the query keeps its binding term), and a non-finite mask weight
+removes that query's binding term (its mask weight reads as 0). The result must
 equal the oracle's on a layout that says the same with valid metadata: the
 bad tokens turned into other tokens, except the target queries with a bad
 time, whose rows are compared with the oracle run without the temporal term.
@@ -50,7 +51,10 @@ def _bad_layout():
     time[bad_time_g] = [np.inf, np.nan, -np.inf]
     bad_pic = rng.choice(pc, 4, replace=False)
     pic[bad_pic] = [3, 40, -1, -7]          # num_pictures is 3
-    raw = ti.Layout(seg, time, pic, lay.frame, lay.mask)
+    bad_mask = rng.choice(np.setdiff1d(tgt, np.concatenate([bad_seg, bad_time_t])), 3, replace=False)
+    mask = lay.mask.copy()
+    mask[bad_mask] = [np.nan, np.inf, -np.inf]
+    raw = ti.Layout(seg, time, pic, lay.frame, mask)
     clean_seg = seg.copy()
     clean_seg[np.concatenate([bad_seg, bad_time_g, bad_pic])] = ti.SEG_OTHER
     clean_time = time.copy()
@@ -58,7 +62,9 @@ def _bad_layout():
     clean_time[bad_time_t] = 0.0          # their rows are checked without the temporal term
     clean_pic = pic.copy()
     clean_pic[clean_seg != ti.SEG_PICTURE] = -1
-    clean = ti.Layout(clean_seg, clean_time, clean_pic, lay.frame, lay.mask)
+    clean_mask = mask.copy()
+    clean_mask[bad_mask] = 0.0            # a non-finite weight drops that query's binding term
+    clean = ti.Layout(clean_seg, clean_time, clean_pic, lay.frame, clean_mask)
     return raw, clean, bad_time_t
 
 

@@ -83,11 +83,14 @@ def test_three_term_segment_extremes():
 
 @pytest.mark.parametrize("cid", [5, 6])
 def test_fullsize_three_term_sampled_rows(cid):
+    """Full sequence length, two heads; the outputs are NaN-poisoned before
+    the call and every element must be written (by the merge of the three
+    term partitions)."""
     cfg = ti.config(cid)
     lay = cfg.layout()
     q, k, v = ti.qkv(cfg, heads=[0, 1])
     rows = sample_rows(lay, n_random=256, per_segment=64, seed=80 + cid)
     log(f"config {cid}: N={lay.n}, three-term, {len(rows)} rows x 2 heads")
-    o, l = run_gpu(q, k, v, lay, cfg.params, mode="three-term", rows=rows)
+    o, l = run_gpu(q, k, v, lay, cfg.params, mode="three-term", rows=rows, poison=True)
     ro, rl = run_oracle(q, k, v, lay, cfg.params, rows=rows)
     compare(o.numpy(), l.numpy(), ro, rl, what=f"config {cid} three-term sampled")

@@ -375,6 +375,37 @@ def test_p9_invariances():
     assert np.max(np.abs(ob[0, 1] - o1)) < 1e-12 and np.max(np.abs(lb[0, 1] - l1)) < 1e-12
 
 
+def test_p9_batched_attention_matches_bruteforce_per_batch():
+    """oracle.attention at B = 2, H = 2, where the two batch elements have
+    different metadata and two chained bindings with their own mask planes
+    ([J, B, N]): every (b, h) equals the pure-Python brute force run on that
+    batch element's own metadata and mask planes. A batch-index slip in the
+    metadata or in the mask planes would mix the two layouts and fail."""
+    rng = np.random.default_rng(57)
+    n, d = 19, 5
+    lays = [ti.random_layout(rng, n, frames=4, pictures=2, mask=True) for _ in range(2)]
+    for lay in lays:
+        assert (lay.seg == ti.SEG_TARGET).any() and (lay.seg == ti.SEG_PICTURE).any()
+    assert not np.array_equal(lays[0].seg, lays[1].seg)
+    # mask planes [J=2, B=2, N]: each batch element's own first plane and a second random plane
+    masks = np.stack([np.stack([lay.mask, rng.uniform(0.0, 1.0, n).astype(np.float32)]) for lay in lays], axis=1)
+    p = ti.Params(window=0.1, falloff=0.3, strength=3.0, cap=5.0, binding=True, gains=(1.9, 0.6),
+                  chained=((0.7, 2.2),))
+    q, k, v = (rng.standard_normal((2, 2, n, d)) for _ in range(3))
+    seg = np.stack([x.seg for x in lays])
+    tim = np.stack([x.time for x in lays])
+    pic = np.stack([x.picture for x in lays])
+    ob, lb = oracle.attention(q, k, v, seg, tim, pic, masks, p)
+    for b in range(2):
+        for h in range(2):
+            bo, bl = oracle.attention_bruteforce(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), lays[b].seg,
+                                                 lays[b].time, lays[b].picture, masks[:, b], p)
+            assert np.max(np.abs(ob[b, h] - bo)) < 1e-12 and np.max(np.abs(lb[b, h] - bl)) < 1e-12
+    # the two batch elements really differ (so a swap would be caught)
+    o_swapped, _ = oracle.attention(q, k, v, seg[::-1], tim[::-1], pic[::-1], masks[:, ::-1], p)
+    assert np.max(np.abs(o_swapped - ob)) > 1e-3
+
+
 # ----------------------------------------------------------- P10: monotonicity
 def test_p10_monotone_guide_mass():
     rng = np.random.default_rng(33)
@@ -557,7 +588,8 @@ def _pins_pass(golden_dir):
               lambda: test_p8_three_term_parts_merge_to_attention("defaults"),
               lambda: test_p12_fp8_e4m3_hand_worked(golden_dir),
               lambda: test_p12_fp8_e4m3_against_code_table(),
-              lambda: test_p12_scales_and_dequantised_error()]
+              lambda: test_p12_scales_and_dequantised_error(),
+              lambda: test_p9_batched_attention_matches_bruteforce_per_batch()]
     for c in checks:
         try:
             c()
@@ -688,6 +720,17 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
         # m = 1 on every target query whatever the mask says
         return real_bias(seg_q, tq, None, seg_k, tk, pk, params)
 
+    real_attention = tor.attention
+
+    def batch0_metadata(q, k, v, seg, time, picture, mask, params, **kw):
+        # every batch element reads batch element 0's metadata and mask planes
+        seg, time, picture = (np.repeat(np.asarray(x)[:1], np.asarray(x).shape[0], axis=0)
+                              for x in (seg, time, picture))
+        if mask is not None:
+            mk = np.asarray(mask)
+            mask = np.repeat(mk[..., :1, :], mk.shape[-2], axis=-2)
+        return real_attention(q, k, v, seg, time, picture, mask, params, **kw)
+
     mutants = [("pow2_scale", scale_one_low), ("qk8_dequantize", per_tensor_k_scale),
                ("penalty", no_cap), ("bias_block", guide_rows_biased_too), ("bias_block", binding_on_every_row),
                ("bias_block", bias_scaled_like_logits), ("bias_block", mask_ignored),
@@ -695,10 +738,11 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
                ("bias_block", swap_qk_roles), ("bias_block", log2_gain), ("attention_head", transposed_kv),
                ("bias_block", first_binding_only), ("bias_block", one_mask_plane),
                ("three_term_parts", correction_keeps_cap), ("fp8_e4m3_round", fp8_truncating),
-               ("fp8_e4m3_round", fp8_half_away)]
+               ("fp8_e4m3_round", fp8_half_away), ("attention", batch0_metadata)]
     for name, fn in mutants:
         with monkeypatch.context() as m:
             m.setattr(tor, name, fn)
-            if name in ("attention_head", "three_term_parts", "fp8_e4m3_round", "pow2_scale", "qk8_dequantize"):
+            if name in ("attention_head", "three_term_parts", "fp8_e4m3_round", "pow2_scale", "qk8_dequantize",
+                        "attention"):
                 m.setattr(oracle, name, fn)
             assert not _pins_pass(golden_dir), f"planted mistake {fn.__name__} went unnoticed"
