@@ -219,6 +219,35 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   const tara_params_t* p, void* workspace, size_t workspace_bytes,
                   tara_stream_t stream);
 
+/* Workspace of tara_attn_fwd_noalloc, in bytes: a fixed device array of the
+ * library (128 MiB on each device it runs on, held until the process ends). */
+#define TARA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* tara_attn_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, rules and results as tara_attn_fwd, without the workspace:
+ * the library's own device array of TARA_NOALLOC_SCRATCH_BYTES serves as the
+ * workspace, and the call is worked through one batch element and as many
+ * heads as that array holds at a time, in order on `stream`, with the same
+ * kernels. Allocates nothing (no hipMalloc, no host allocation on the call
+ * path). The first call on a device looks the array's device address up once.
+ * Every call on one device shares that device's array and leaves its last
+ * contents there (nothing in it has to start at zero): calls that overlap on
+ * one device (on different streams, or from threads not ordered on one
+ * stream) race and give wrong results; calls in order on one stream do not.
+ * Errors: as tara_attn_fwd, plus TARA_ERR_WORKSPACE when one head of one batch
+ * element needs more workspace than the array holds (for instance the
+ * DENSE_BIAS baseline beyond about 5,000 tokens). This entry point does not
+ * record timing events and ignores TARA_VALIDATE and the tile-class readback,
+ * which synchronise or allocate. */
+int tara_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          tara_dtype_t dtype, int B, int H, int N, int D,
+                          const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
+                          const int64_t o_str[3],
+                          const uint8_t* seg_type, const float* token_time,
+                          const int16_t* picture_id, const float* mask_weight,
+                          const tara_params_t* p, tara_stream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* tara_status_string(int status);
 

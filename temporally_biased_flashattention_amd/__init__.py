@@ -25,7 +25,7 @@ __all__ = [
     "TARA_BF16", "TARA_FP32", "TARA_MODE_FUSED", "TARA_MODE_PARTITIONED", "TARA_MODE_THREE_TERM",
     "TARA_MODE_DENSE_BIAS", "TARA_MODE_FRAME_LOOP", "TARA_PROBE_CONSTANT", "TARA_PROBE_RANDOM",
     "TaraError", "TaraLibraryMissing", "TaraParams", "TaraRunInfo",
-    "tara_params_default", "make_params", "tara_workspace_bytes", "tara_attn_fwd",
+    "tara_params_default", "make_params", "tara_workspace_bytes", "tara_attn_fwd", "tara_attn_fwd_noalloc",
     "tara_status_string", "tara_last_error", "tara_get_last_run_info",
     "tara_timing_enable", "tara_timing_read", "tara_probe_mfma_bf16", "attn_fwd", "library_path",
     "load_library",
@@ -43,7 +43,7 @@ TARA_MAX_PARTITIONS = 64
 EXPORTED_SYMBOLS = (
     "tara_params_default", "tara_workspace_bytes", "tara_attn_fwd", "tara_status_string",
     "tara_last_error", "tara_get_last_run_info", "tara_timing_enable", "tara_timing_read",
-    "tara_probe_mfma_bf16",
+    "tara_probe_mfma_bf16", "tara_attn_fwd_noalloc",
 )
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -116,6 +116,10 @@ def load_library():
                                    ctypes.c_int, I64_3, I64_3, I64_3, I64_3, P, P, P, P,
                                    ctypes.POINTER(TaraParams), P, ctypes.c_size_t, P])
     lib.tara_attn_fwd.restype = ctypes.c_int
+    lib.tara_attn_fwd_noalloc.argtypes = ([P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, I64_3, I64_3, I64_3, I64_3, P, P, P, P,
+                                           ctypes.POINTER(TaraParams), P])
+    lib.tara_attn_fwd_noalloc.restype = ctypes.c_int
     lib.tara_status_string.argtypes = [ctypes.c_int]
     lib.tara_status_string.restype = ctypes.c_char_p
     lib.tara_last_error.argtypes = []
@@ -285,6 +289,27 @@ def tara_attn_fwd(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight
         _strides(q), _strides(k), _strides(v), _strides(o),
         _ptr(seg_type), _ptr(token_time), _ptr(picture_id), _ptr(mask_weight),
         ctypes.byref(params), _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    _check(st)
+
+
+def tara_attn_fwd_noalloc(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight,
+                          params: TaraParams, stream=None) -> None:
+    """Calls tara_attn_fwd_noalloc: tara_attn_fwd without a workspace (the
+    library's fixed device array serves as one; see include/tara.h). Same
+    tensor rules as tara_attn_fwd."""
+    import torch
+    _check_call_args(q, k, v, o, lse, seg_type, token_time, picture_id, mask_weight, params, None)
+    lib = load_library()
+    B, H, N, D = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    elif stream.device != q.device:
+        raise ValueError(f"stream is on {stream.device}, q is on {q.device}")
+    st = lib.tara_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), B, H, N, D,
+        _strides(q), _strides(k), _strides(v), _strides(o),
+        _ptr(seg_type), _ptr(token_time), _ptr(picture_id), _ptr(mask_weight),
+        ctypes.byref(params), ctypes.c_void_p(stream.cuda_stream))
     _check(st)
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtara.so")
-SOURCES = ["tara_kernels.hip", "tara_host.cpp", "tara_probe.hip"]
+SOURCES = ["tara_kernels.hip", "tara_host.cpp", "tara_probe.hip", "tara_noalloc.hip"]
 ARCH = "gfx950"
 
 
