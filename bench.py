@@ -121,6 +121,113 @@ def cpu_model() -> str:
     return "unknown"
 
 
+class ClockSampler:
+    """Samples the GPU's current shader (GFX) clock through amdsmi every
+    `period` seconds in a background thread while the timed steps run; the
+    clock the chip settles at under the load (it is power-limited) sets how
+    much of the nominal peak the kernel can reach. Reports nothing if amdsmi
+    is unavailable."""
+
+    def __init__(self, period: float = 0.02):
+        self.period = period
+        self.samples = []
+        self.error = None
+        self._stop = None
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._amdsmi = amdsmi
+            self._handle = handles[0] if handles else None
+            if self._handle is None:
+                self.error = "no GPU handle"
+        except Exception as e:  # noqa: BLE001
+            self.error = f"amdsmi unavailable: {e}"
+
+    def _read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info.get("clk", info.get("cur_clk")))
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # noqa: BLE001
+                self.error = f"clock read failed: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._handle is not None:
+            self._stop = threading.Event()
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return {"median": None, "samples": 0, "source": "amdsmi GFX clock", "error": self.error}
+        xs = sorted(self.samples)
+        return {"median": xs[len(xs) // 2], "min": xs[0], "max": xs[-1], "samples": len(xs),
+                "source": "amdsmi GFX clock, sampled during the timed steps"}
+
+
+def oracle_configs(seconds: float):
+    """Times the fp64 oracle (as it stands) on every workload, on this host's
+    cores: workloads 1 and 2 on all rows and heads, the larger ones on a
+    bounded stratified row sample of head 0, extrapolated linearly to all
+    rows and heads. One JSON line per workload."""
+    import numpy as np
+
+    import oracle
+    import tara_inputs as ti
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 0)) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    for cid in (1, 2, 3, 4, 5, 6, 7):
+        cfg = ti.config(cid)
+        lay = cfg.layout()
+        n, h, d = lay.n, cfg.heads, cfg.head_dim
+        p = cfg.params.f32()
+        full = cid in (1, 2)
+        t0 = time.perf_counter()
+        if full:
+            q, k, v = ti.qkv(cfg)
+            for hh in range(h):
+                oracle.attention_head(q[0, hh].float().numpy(), k[0, hh].float().numpy(), v[0, hh].float().numpy(),
+                                      lay.seg, lay.time, lay.picture, lay.mask, p)
+            rows, heads = n, h
+        else:
+            q, k, v = ti.qkv(cfg, heads=[0])
+            rs = np.random.default_rng(3).permutation(ti.sample_rows(lay, n_random=30000, per_segment=512, seed=3))
+            qh, kh, vh = (x[0, 0].float().numpy() for x in (q, k, v))
+            done = 0
+            while done < len(rs) and time.perf_counter() - t0 < seconds:
+                r = np.sort(rs[done:done + 256])
+                oracle.attention_head(qh, kh, vh, lay.seg, lay.time, lay.picture, lay.mask, p, rows=r)
+                done += len(r)
+            rows, heads = done, 1
+        dt = time.perf_counter() - t0
+        total = dt * (n / rows) * (h / heads)
+        print(json.dumps({"workload": cfg.name, "tokens": n, "heads": h, "head_dim": d,
+                          "oracle_s_per_call": round(total, 1), "timed_s": round(dt, 1),
+                          "timed": "all rows and heads" if full else f"{rows} stratified rows of head 0, "
+                                                                    "extrapolated to all rows and heads",
+                          "tflops": round(attention_flop(1, heads, rows, n, d) / dt / 1e12, 4),
+                          "cores": cores, "cpu": cpu_model(), "host_cpus": os.cpu_count()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +242,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
+    ap.add_argument("--oracle-configs", action="store_true",
+                    help="time the fp64 oracle on every workload on this host's cores (no GPU used) and exit")
     args = ap.parse_args()
+    if args.oracle_configs:
+        oracle_configs(args.cpu_seconds)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); "
@@ -186,15 +298,22 @@ def main():
         log(f"warmup {i + 1}/{args.warmup} done")
     tara.tara_timing_read()
     tara.tara_timing_enable(True)
+    # per-step HIP events on the stream the library launches on (torch's current one)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        evs[0].record()
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     tara.tara_timing_enable(False)
     kms = tara.tara_timing_read()
-    log(f"{args.steps} timed steps in {elapsed:.3f} s")
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    log(f"{args.steps} timed steps in {elapsed:.3f} s; step median {step_ms[len(step_ms) // 2]:.3f} ms, "
+        f"min {step_ms[0]:.3f} ms; GFX clock {clock.summary()}")
     info = tara.tara_get_last_run_info()
     # the bf16 MFMA rates this box sustains with nothing else to do, right after the timed
     # steps: on varied operands (power-limited, the practical ceiling on real data) and on
@@ -236,6 +355,10 @@ def main():
         "dtype": "fp8 (Q.K) + bf16 (P.V)" if args.qk8 else cfg.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, packed H3-shaped metadata)",
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        # each timed step from HIP events around it on the stream (the whole call)
+        "step_ms": {"mean": round(ms_step, 3), "median": round(step_ms[len(step_ms) // 2], 3),
+                    "min": round(step_ms[0], 3), "max": round(step_ms[-1], 3)},
+        "gfx_clock_mhz": clock.summary(),
         "config": {"workload": f"{cfg.name} ({args.mode}{', 8-bit Q.K' if args.qk8 else ''})", "tokens": N, "heads": H, "head_dim": D, "batch": B,
                    "target_tokens": int((lay.seg == 0).sum()), "guide_tokens": int((lay.seg == 1).sum()),
                    "mode": args.mode, "partitions": info.get("num_partitions"), "qk8": args.qk8,
@@ -248,6 +371,8 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
                      "kernel_ms_avg": round(k_avg, 4), "launches_timed": len(kms),
+                     "kernel_ms_median": round(sorted(kms)[len(kms) // 2], 4) if kms else None,
+                     "kernel_ms_min": round(min(kms), 4) if kms else None,
                      "flop_per_launch": flop,
                      # back-to-back bf16 MFMAs on register operands, same box: varied operands
                      # (power-limited like the kernel's own products) and constant ones

@@ -171,7 +171,7 @@ void tara_params_default(tara_params_t* p);
  * call (B, H or N == 0) and (size_t)-1 for arguments tara_attn_fwd would reject
  * (p == NULL, bad dtype or head dim, bad partition count, qk8 outside bf16
  * fused mode, DENSE_BIAS with fp32). */
-size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
+size_t tara_workspace_bytes(int dtype, int B, int H, int N, int D,
                             const tara_params_t* p);
 
 /* TARA-biased attention forward: O = softmax(logits) V and LSE per query row.
@@ -185,7 +185,10 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
  *           (else TARA_ERR_BAD_STRIDE).
  *  o        device, same dtype and layout rules (strides o_str); fully written.
  *  lse      device fp32 [B][H][N] contiguous, natural log; fully written.
- *  dtype    TARA_BF16 (bf16 in and out, fp32 accumulation) or TARA_FP32.
+ *  dtype    a tara_dtype_t value: TARA_BF16 (bf16 in and out, fp32
+ *           accumulation) or TARA_FP32; any other int is rejected (the
+ *           parameter is an int so that every value a caller may pass is
+ *           well defined).
  *  D        64 or 128.
  *  seg_type device uint8 [B][N], TARA_SEG_* codes.
  *  token_time device fp32 [B][N], seconds on the aligned output clock; read
@@ -211,7 +214,7 @@ size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D,
  * first (synchronously), returning TARA_ERR_BAD_METADATA.
  * B, H or N == 0 is a valid empty call and enqueues nothing. */
 int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                  tara_dtype_t dtype, int B, int H, int N, int D,
+                  int dtype, int B, int H, int N, int D,
                   const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
                   const int64_t o_str[3],
                   const uint8_t* seg_type, const float* token_time,
@@ -241,7 +244,7 @@ int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
  * record timing events and ignores TARA_VALIDATE and the tile-class readback,
  * which synchronise or allocate. */
 int tara_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
-                          tara_dtype_t dtype, int B, int H, int N, int D,
+                          int dtype, int B, int H, int N, int D,
                           const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
                           const int64_t o_str[3],
                           const uint8_t* seg_type, const float* token_time,

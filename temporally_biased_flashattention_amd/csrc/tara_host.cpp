@@ -212,12 +212,13 @@ void set_empty_info(const Call& c) {
   set_last_info(info);
 }
 
-int make_call(Call& c, const void* q, const void* k, const void* v, void* o, float* lse, tara_dtype_t dtype, int B,
+int make_call(Call& c, const void* q, const void* k, const void* v, void* o, float* lse, int dtype_, int B,
               int H, int N, int D, const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
               const int64_t o_str[3], const uint8_t* seg_type, const float* token_time, const int16_t* picture_id,
               const float* mask_weight, const tara_params_t* p) {
   if (!p) return fail(TARA_ERR_NULL_POINTER, "params are NULL");
-  if (dtype != TARA_BF16 && dtype != TARA_FP32) return fail(TARA_ERR_UNSUPPORTED_DTYPE, "dtype must be TARA_BF16 or TARA_FP32");
+  if (dtype_ != TARA_BF16 && dtype_ != TARA_FP32) return fail(TARA_ERR_UNSUPPORTED_DTYPE, "dtype must be TARA_BF16 or TARA_FP32");
+  const tara_dtype_t dtype = (tara_dtype_t)dtype_;
   if (D != 64 && D != 128) return fail(TARA_ERR_UNSUPPORTED_HEAD_DIM, "head dim must be 64 or 128");
   if (B < 0 || H < 0 || N < 0) return fail(TARA_ERR_BAD_SHAPE, "B, H and N must be >= 0");
   if ((int64_t)B * H > 65535) return fail(TARA_ERR_BAD_SHAPE, "B * H must be <= 65535");
@@ -575,8 +576,9 @@ void tara_params_default(tara_params_t* p) {
   p->partition_bounds = nullptr;
 }
 
-size_t tara_workspace_bytes(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
-  if (!p || (dtype != TARA_BF16 && dtype != TARA_FP32) || (D != 64 && D != 128)) return (size_t)-1;
+size_t tara_workspace_bytes(int dtype_, int B, int H, int N, int D, const tara_params_t* p) {
+  if (!p || (dtype_ != TARA_BF16 && dtype_ != TARA_FP32) || (D != 64 && D != 128)) return (size_t)-1;
+  const tara_dtype_t dtype = (tara_dtype_t)dtype_;
   if (B < 0 || H < 0 || N < 0) return (size_t)-1;
   if (p->mode == TARA_MODE_PARTITIONED && (p->num_partitions < 1 || p->num_partitions > TARA_MAX_PARTITIONS))
     return (size_t)-1;
@@ -636,7 +638,7 @@ int tara_timing_read(float* ms_out, int max, int* count) {
   return status;
 }
 
-int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, tara_dtype_t dtype,
+int tara_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
                   int B, int H, int N, int D, const int64_t q_str[3], const int64_t k_str[3],
                   const int64_t v_str[3], const int64_t o_str[3], const uint8_t* seg_type,
                   const float* token_time, const int16_t* picture_id, const float* mask_weight,

@@ -168,7 +168,7 @@ struct Call {
 };
 // Checks the arguments of tara_attn_fwd (everything but the workspace) and
 // fills c; a nonzero status (with the thread's last error set) on failure.
-int make_call(Call& c, const void* q, const void* k, const void* v, void* o, float* lse, tara_dtype_t dtype, int B,
+int make_call(Call& c, const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int B,
               int H, int N, int D, const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
               const int64_t o_str[3], const uint8_t* seg_type, const float* token_time, const int16_t* picture_id,
               const float* mask_weight, const tara_params_t* p);

@@ -51,7 +51,7 @@ int scratch_ptr(void** out) {
 }  // namespace
 
 extern "C" int tara_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
-                                     tara_dtype_t dtype, int B, int H, int N, int D, const int64_t q_str[3],
+                                     int dtype, int B, int H, int N, int D, const int64_t q_str[3],
                                      const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
                                      const uint8_t* seg_type, const float* token_time, const int16_t* picture_id,
                                      const float* mask_weight, const tara_params_t* p, tara_stream_t stream_) {
