@@ -107,11 +107,12 @@ def test_qk8_zero_rows_and_ragged_tail():
     check_qk8(q, k, v, lay, ti.Params(), "qk8 zero rows / tile, ragged")
 
 
-@pytest.mark.parametrize("cid", [2, 6])
+@pytest.mark.parametrize("cid", [2, 5, 6])
 def test_qk8_fullsize_sampled(cid):
     """One fused 8-bit call over all heads at full size: workload 2 (54,272
-    tokens x 8 heads) and the benchmark workload 6 (107,126 tokens x 56
-    heads, D 128); stratified rows of three heads."""
+    tokens x 8 heads), the binding workload 5 (107,682 tokens x 56 heads,
+    three pictures, a soft mask) and the benchmark workload 6 (107,126 tokens
+    x 56 heads, D 128); stratified rows of three heads."""
     cfg = ti.config(cid)
     lay = cfg.layout()
     log(f"config {cid} {cfg.name}: N={lay.n} H={cfg.heads}; generating inputs")
