@@ -1,8 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (all heads, one fused call; partitioned for the binding
 workload too), against the fp64 oracle: stratified samples of query rows on
-three heads, 64 stratified rows on every head, and one head of the benchmark
-workload on all 107,126 rows. The outputs are NaN-poisoned before each call
+three heads, 64 stratified rows on every head, and one head each of the
+benchmark workload and of the binding workload on all rows. The outputs are NaN-poisoned before each call
 and every element of them must be written. Full-scale Q = 0 probes make the
 attention weights a function of the bias alone, so per-segment attention mass
 checks the temporal and binding terms at full size with a tight gate.
@@ -72,14 +72,16 @@ def test_fullsize_sampled_rows(cid):
             what=f"config {cid} fused, 64 rows on every one of {cfg.heads} heads")
 
 
-def test_fullsize_all_rows_one_head():
-    """The benchmark workload (107,126 tokens x 56 heads, d128) in one fused
-    call with poisoned outputs; head 27 compared with the oracle on all
-    107,126 rows (about 6e12 fp64 FLOP on the host)."""
-    cfg = ti.config(6)
+@pytest.mark.parametrize("cid,h", [(6, 27), (5, 41)])
+def test_fullsize_all_rows_one_head(cid, h):
+    """One fused call with poisoned outputs, one head compared with the oracle
+    on every row (about 6e12 fp64 FLOP on the host each): the benchmark
+    workload 6 (107,126 tokens x 56 heads, d128) at head 27, and the binding
+    workload 5 (107,682 tokens x 56 heads, three pictures, a soft mask) at
+    head 41."""
+    cfg = ti.config(cid)
     lay = cfg.layout()
     q, k, v = ti.qkv(cfg)
-    h = 27
     o, l = run_gpu(q, k, v, lay, cfg.params, heads=[h], poison=True)
     blk = 8192
     ro = np.zeros((1, 1, lay.n, cfg.head_dim))
@@ -88,7 +90,7 @@ def test_fullsize_all_rows_one_head():
         rows = np.arange(r0, min(r0 + blk, lay.n))
         ro[:, :, rows], rl[:, :, rows] = run_oracle(q, k, v, lay, cfg.params, rows=rows, heads=[h])
         log(f"oracle head {h}: rows {r0}..{rows[-1]} done")
-    compare(o.numpy(), l.numpy(), ro, rl, what=f"config 6 head {h}, all {lay.n} rows")
+    compare(o.numpy(), l.numpy(), ro, rl, what=f"config {cid} head {h}, all {lay.n} rows")
 
 
 @pytest.mark.parametrize("d", [64, 128])
