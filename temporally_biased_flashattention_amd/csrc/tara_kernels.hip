@@ -382,6 +382,13 @@ __device__ __forceinline__ void dma16(BufRange r, uint32_t voff, uint32_t soff, 
       (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
+// Chunk swizzle of the V^T tile in LDS: the 16-byte chunk c of V^T row r (8
+// chunks of a 64-key row, no padding) sits at position c ^ vswz(r). The 16
+// lanes of a fragment read that take rows r0 .. r0 + 15 (same chunk) then hit
+// 16 different 16-byte bank groups: row r's bytes start at bank group
+// 8 * (r & 1), and vswz covers (r >> 1) & 7.
+__device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
+
 // Tile staging by LDS DMA (buffer_load_dwordx4 ... lds): one wave instruction
 // writes 64 lanes x 16 bytes contiguously at a uniform LDS address. A padded
 // tile of BLK whole 1-KB blocks (rows of ROWB bytes holding DATA 16-byte data
@@ -392,7 +399,7 @@ __device__ __forceinline__ void dma16(BufRange r, uint32_t voff, uint32_t soff, 
 // bytes save). Buffer loads rather than global_load_lds: the latter is
 // FLAT-encoded, and while one is in flight the compiler cannot count LDS
 // reads, so every fragment wait would drain all of them.
-template <int ROWB, int DATA, int BLK, int NW>
+template <int ROWB, int DATA, int BLK, int NW, bool SWZ = false>
 struct TileDma {
   static constexpr int PER_MIN = BLK / NW;
   static constexpr int PER_MAX = (BLK + NW - 1) / NW;
@@ -406,7 +413,8 @@ struct TileDma {
       const int ci = min(wave + p * NW, BLK - 1);
       const int o = ci * 1024 + lane * 16, r = o / ROWB, c = (o % ROWB) / 16;
       row[p] = r;
-      voff[p] = r * row_bytes + (c < DATA ? c * 16 : 0);
+      // SWZ: LDS chunk c of row r holds the row's chunk c ^ vswz(r)
+      voff[p] = r * row_bytes + (SWZ ? (c ^ vswz(r)) * 16 : c < DATA ? c * 16 : 0);
     }
   }
   // Stage the tile at byte offset soff of r into lds (wave in [0, NW)). With
@@ -453,10 +461,12 @@ __device__ __forceinline__ bf16x8 kfrag(const __bf16* kr0, int i) {
 }
 
 // i-th V^T fragment of phase B: 32-row block i % NDB of the head dim, 16-key
-// chunk i / NDB (key block kb = chunk / 2, half c2 = chunk % 2).
+// chunk i / NDB (key block kb = chunk / 2, half c2 = chunk % 2). vr0 is the
+// lane's row (db = 0) and vck[chunk] the element offset of its 16 bytes of
+// that chunk in the swizzled row.
 template <int VROW, int NDB>
-__device__ __forceinline__ bf16x8 vfrag(const __bf16* vr0, int i) {
-  return *reinterpret_cast<const bf16x8*>(vr0 + (i % NDB) * 32 * VROW + (i / NDB) * 16);
+__device__ __forceinline__ bf16x8 vfrag(const __bf16* vr0, const int (&vck)[4], int i) {
+  return *reinterpret_cast<const bf16x8*>(vr0 + (i % NDB) * 32 * VROW + vck[i / NDB]);
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -652,7 +662,11 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int KROW = D + 8;              // padded LDS pitch of a bf16 K row (elements)
   // LDS pitch of a K row in bytes (FP8 rows: D bytes + a 16-byte pad)
   constexpr int KROWB = Q8 ? D + 16 : KROW * 2;
-  constexpr int VROW = kBlockK + 8;        // padded LDS pitch of a V^T row (elements)
+  // V^T rows in LDS: swizzled 16-byte chunks without padding (vswz), except in
+  // the dense-bias baseline, whose bias loads leave no registers for the four
+  // per-lane chunk offsets the swizzle needs: there rows are padded by 16 bytes
+  constexpr bool VSWZ = !DB;
+  constexpr int VROW = VSWZ ? kBlockK : kBlockK + 8;   // LDS pitch of a V^T row (elements)
   constexpr int KTILE = kBlockK * KROWB / 2;   // K tile size in bf16 elements
   constexpr int VTILE = D * VROW;
   constexpr int NKK = D / 16;
@@ -845,7 +859,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const BufRange rv{vg, (uint32_t)(D * a.npad * 2)};
   static_assert(KTILE * 2 % 1024 == 0 && VTILE * 2 % 1024 == 0, "tiles are whole 1-KB blocks");
   using KDma = TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW>;
-  using VDma = TileDma<VROW * 2, kBlockK / 8, VTILE * 2 / 1024, NW>;
+  using VDma = TileDma<VROW * 2, kBlockK / 8, VTILE * 2 / 1024, NW, VSWZ>;
   KDma kdma;
   VDma vdma;
   kdma.init(wave, lane, k_sn_bytes);
@@ -897,7 +911,12 @@ void attn_bf16_kernel(AttnArgs a) {
   i32x8 kf8[2];
   const int koff_lane = krow_lane * KROW + hh * 8;   // phase A reads K rows kb*32 + perm32(lq)
   const int koffb8 = krow_lane * KROWB + hh * 32;    // the same rows, FP8 bytes
-  const int voff_lane = lq * VROW + hh * 8;          // phase B reads V^T rows db*32 + lq
+  const int voff_lane = lq * VROW + (VSWZ ? 0 : hh * 8);   // phase B reads V^T rows db*32 + lq
+  // element offsets of the lane's 16 bytes of 16-key chunk kc (keys 16*kc + 8*hh
+  // .. +7) in its V^T row (swizzled: rows db*32 + lq share vswz, as 32 | db*32)
+  int vck[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) vck[kc] = VSWZ ? ((2 * kc + hh) ^ vswz(lq)) * 8 : kc * 16;
   // raw Q.K products to log2 units for a tile (cq: the row part; times the tile's scale)
   auto tile_mul = [&](float kscale) { return Q8 ? cq * kscale : a.c; };
   // dense-bias baseline: this row of the bias tensor (pitch npad floats);
@@ -1058,9 +1077,9 @@ void attn_bf16_kernel(AttnArgs a) {
         if (i + 1 < NA) {
           kf8[(i + 1) & 1] = kfrag8<KROWB>(k8r, i + 1);
         } else {
-          fr[0] = vfrag<VROW, NDB>(vr0, 0);
-          fr[1] = vfrag<VROW, NDB>(vr0, 1);
-          fr[2] = vfrag<VROW, NDB>(vr0, 2);
+          fr[0] = vfrag<VROW, NDB>(vr0, vck, 0);
+          fr[1] = vfrag<VROW, NDB>(vr0, vck, 1);
+          fr[2] = vfrag<VROW, NDB>(vr0, vck, 2);
         }
         sn[i & 1] = mfma_fp8(kf8[i & 1], qf8[i >> 1], sn[i & 1]);
 #pragma unroll
@@ -1072,7 +1091,7 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int i = 0; i < NA; ++i) {
         const int j = i + 3;
         if (j < NA) fr[j & 3] = kfrag<KROW>(kr0, j);
-        else fr[j & 3] = vfrag<VROW, NDB>(vr0, j - NA);
+        else fr[j & 3] = vfrag<VROW, NDB>(vr0, vck, j - NA);
         sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
         if (i < 16) exp_only(i);
         if (i >= 1 && i <= 16) pack_pair(i - 1);
@@ -1138,7 +1157,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int j = i + 3;
-      if (j < NB) fr[j & 3] = vfrag<VROW, NDB>(vr0, j);
+      if (j < NB) fr[j & 3] = vfrag<VROW, NDB>(vr0, vck, j);
       else if (!Q8) fr[j & 3] = kfrag<KROW>(kn0, j - NB);
       else if (j == NB) kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(s2)) + koffb8, 0);
       const int db = i % NDB, kc = i / NDB;
