@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tara_internal.h"
 
 namespace tara {
@@ -432,6 +434,43 @@ struct TileDma {
   }
 };
 
+// The bf16 K tile at head dim 128 without row padding: 16 blocks of 4 rows (1 KB
+// each, one DMA each: exactly two per wave of eight), block b at LDS byte
+// b * kKBlkPitch (the last 64 bytes of each pitch are never written), and the
+// 16-byte chunk c of row r at chunk position c ^ (r & 3). The 16 lanes of a
+// fragment read take 16 consecutive rows at one chunk: their 16-byte bank
+// groups (4 * block + position) mod 16 are all different.
+constexpr int kKBlkPitch = 1024 + 64;
+template <int NW>
+struct KTileDmaBlk {
+  static constexpr int BLK = 16;
+  static constexpr int PER_MIN = BLK / NW;
+  static constexpr int PER_MAX = (BLK + NW - 1) / NW;
+  static constexpr int NEXTRA = BLK % NW;
+  uint32_t voff[PER_MAX];   // byte offset of this lane's 16 bytes in its tile
+  int row[PER_MAX];         // tile row of those bytes
+  __device__ void init(int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+    for (int p = 0; p < PER_MAX; ++p) {
+      const int b = min(wave + p * NW, BLK - 1);
+      const int r = 4 * b + (lane >> 4), pos = lane & 15;
+      row[p] = r;
+      voff[p] = r * row_bytes + (pos ^ (r & 3)) * 16;
+    }
+  }
+  // as TileDma::issue (TAIL: rows at or past rows_left re-read row rows_left - 1)
+  template <bool TAIL>
+  __device__ void issue(BufRange rg, uint32_t soff, int rows_left, uint32_t row_bytes, char* lds, int wave) const {
+#pragma unroll
+    for (int p = 0; p < PER_MAX; ++p) {
+      if (p >= PER_MIN && wave >= NEXTRA) break;
+      uint32_t vo = voff[p];
+      if (TAIL) vo -= (uint32_t)(row[p] - min(row[p], rows_left - 1)) * row_bytes;
+      dma16(rg, vo, soff, lds + (wave + p * NW) * kKBlkPitch);
+    }
+  }
+};
+
 // Wait until at most KEEP of this wave's vector-memory operations are pending
 // (the newest KEEP DMAs may stay in flight).
 template <int KEEP>
@@ -439,25 +478,26 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KEEP) : "memory");
 }
 
+// i-th K fragment of phase A: key block i & 1, head-dim step i >> 1, from the
+// K tile at kbuf. kl[kk & 1] is the lane's element offset for even / odd steps
+// kk (they differ in the block layout of KTileDmaBlk), KBS the element
+// distance between the two 32-row key blocks; step kk adds 16 elements.
+template <int KBS>
+__device__ __forceinline__ bf16x8 kfrag(const __bf16* kbuf, const int (&kl)[2], int i) {
+  return *reinterpret_cast<const bf16x8*>(kbuf + (i & 1) * KBS + kl[(i >> 1) & 1] + (i >> 1) * 16);
+}
+
 // S^T for the two 32-key blocks of a K tile in LDS.
-template <int D, int KROW>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const __bf16* ks, int krow_lane, int hh,
+template <int D, int KBS>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const __bf16* kbuf, const int (&kl)[2],
                                         const bf16x8 (&qf)[D / 16]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     s[kb] = f32x16{};
-    const __bf16* kr = ks + (kb * 32 + krow_lane) * KROW + hh * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + kk * 16), qf[kk],
-                                                      s[kb], 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag<KBS>(kbuf, kl, 2 * kk + kb), qf[kk], s[kb], 0, 0, 0);
   }
-}
-
-// i-th K fragment of phase A: key block i & 1, head-dim step i >> 1.
-template <int KROW>
-__device__ __forceinline__ bf16x8 kfrag(const __bf16* kr0, int i) {
-  return *reinterpret_cast<const bf16x8*>(kr0 + (i & 1) * 32 * KROW + (i >> 1) * 16);
 }
 
 // i-th V^T fragment of phase B: 32-row block i % NDB of the head dim, 16-key
@@ -662,6 +702,10 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int KROW = D + 8;              // padded LDS pitch of a bf16 K row (elements)
   // LDS pitch of a K row in bytes (FP8 rows: D bytes + a 16-byte pad)
   constexpr int KROWB = Q8 ? D + 16 : KROW * 2;
+  // bf16 K at D = 128: unpadded rows in blocks (KTileDmaBlk); the same tile size
+  constexpr bool KBLK = !Q8 && D == 128;
+  static_assert(!KBLK || 16 * kKBlkPitch == kBlockK * KROW * 2, "the block layout keeps the tile size");
+  constexpr int KBS = KBLK ? 8 * kKBlkPitch / 2 : 32 * KROW;   // elements between the two 32-row key blocks
   // V^T rows in LDS: swizzled 16-byte chunks without padding (vswz), except in
   // the dense-bias baseline, whose bias loads leave no registers for the four
   // per-lane chunk offsets the swizzle needs: there rows are padded by 16 bytes
@@ -858,7 +902,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const BufRange rk{kg, Q8 ? (uint32_t)(a.npad * D) : (uint32_t)(N - 1) * k_sn_bytes + D * 2};
   const BufRange rv{vg, (uint32_t)(D * a.npad * 2)};
   static_assert(KTILE * 2 % 1024 == 0 && VTILE * 2 % 1024 == 0, "tiles are whole 1-KB blocks");
-  using KDma = TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW>;
+  using KDma = std::conditional_t<KBLK, KTileDmaBlk<NW>, TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW>>;
   using VDma = TileDma<VROW * 2, kBlockK / 8, VTILE * 2 / 1024, NW, VSWZ>;
   KDma kdma;
   VDma vdma;
@@ -909,7 +953,18 @@ void attn_bf16_kernel(AttnArgs a) {
   // with 8-bit Q.K the K fragments (32 bytes each) go through kf8 instead
   bf16x8 fr[4];
   i32x8 kf8[2];
-  const int koff_lane = krow_lane * KROW + hh * 8;   // phase A reads K rows kb*32 + perm32(lq)
+  // phase A reads K rows kb*32 + perm32(lq): the lane's element offsets for even
+  // and odd head-dim steps (equal unless KBLK: there row r's chunk 2*kk + hh sits
+  // at position (2*kk + hh) ^ (r & 3), 16 elements later or earlier)
+  int kl[2];
+  if (KBLK) {
+    const int i_in = krow_lane & 3, b1 = i_in >> 1;
+    const int base = (krow_lane >> 2) * (kKBlkPitch / 2) + i_in * D + 8 * (hh ^ (i_in & 1));
+    kl[0] = base + 16 * b1;
+    kl[1] = base - 16 * b1;
+  } else {
+    kl[0] = kl[1] = krow_lane * KROW + hh * 8;
+  }
   const int koffb8 = krow_lane * KROWB + hh * 32;    // the same rows, FP8 bytes
   const int voff_lane = lq * VROW + (VSWZ ? 0 : hh * 8);   // phase B reads V^T rows db*32 + lq
   // element offsets of the lane's 16 bytes of 16-key chunk kc (keys 16*kc + 8*hh
@@ -952,7 +1007,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < NA; ++i) x[i & 1] = mfma_fp8(kfrag8<KROWB>(k8r, i), qf8[i >> 1], x[i & 1]);
     } else {
-      qk_tile<D, KROW>(x, KBUF(0), krow_lane, hh, qf);
+      qk_tile<D, KBS>(x, KBUF(0), kl, qf);
     }
     const int kbase = tile0 * kBlockK;
     const bool partial = a.elem_all || kbase < k0 || kbase + kBlockK > k1;
@@ -990,10 +1045,10 @@ void attn_bf16_kernel(AttnArgs a) {
     if constexpr (Q8) {
       kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(1)) + koffb8, 0);
     } else {
-      const __bf16* kr0 = KBUF(1) + koff_lane;
-      fr[0] = kfrag<KROW>(kr0, 0);
-      fr[1] = kfrag<KROW>(kr0, 1);
-      fr[2] = kfrag<KROW>(kr0, 2);
+      const __bf16* kr0 = KBUF(1);
+      fr[0] = kfrag<KBS>(kr0, kl, 0);
+      fr[1] = kfrag<KBS>(kr0, kl, 1);
+      fr[2] = kfrag<KBS>(kr0, kl, 2);
     }
     // every wave is done with K slot 0 before iteration t0 restages it
     __builtin_amdgcn_s_barrier();
@@ -1042,9 +1097,9 @@ void attn_bf16_kernel(AttnArgs a) {
       cls_elem = wave_any(lane_elem);
       cls_bound = wave_any(fmaf(qn_c, kmax1, brow) > m_used + kRescaleTau);
     }
-    const __bf16* kr0 = KBUF(s1) + koff_lane;   // K_{t+1}
+    const __bf16* kr0 = KBUF(s1);   // K_{t+1}
     const __bf16* vr0 = VBUF(s0) + voff_lane;   // V_t
-    const __bf16* kn0 = KBUF(s2) + koff_lane;   // K_{t+2}
+    const __bf16* kn0 = KBUF(s2);   // K_{t+2}
 
     // phase A: S_{t+1} = K_{t+1} Q^T (the two 32-key blocks alternate) |
     // P_t = exp2(X_t) in place and its bf16 pack. The ring runs three
@@ -1090,7 +1145,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int j = i + 3;
-        if (j < NA) fr[j & 3] = kfrag<KROW>(kr0, j);
+        if (j < NA) fr[j & 3] = kfrag<KBS>(kr0, kl, j);
         else fr[j & 3] = vfrag<VROW, NDB>(vr0, vck, j - NA);
         sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
         if (i < 16) exp_only(i);
@@ -1158,7 +1213,7 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < NB; ++i) {
       const int j = i + 3;
       if (j < NB) fr[j & 3] = vfrag<VROW, NDB>(vr0, vck, j);
-      else if (!Q8) fr[j & 3] = kfrag<KROW>(kn0, j - NB);
+      else if (!Q8) fr[j & 3] = kfrag<KBS>(kn0, kl, j - NB);
       else if (j == NB) kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(s2)) + koffb8, 0);
       const int db = i % NDB, kc = i / NDB;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
