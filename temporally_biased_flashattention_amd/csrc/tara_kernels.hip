@@ -519,13 +519,15 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 k8, i32x8 q8, f32x16 acc) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k8, q8, acc, 0, 0, 0, 127, 0, 127);
 }
 
-// i-th fp8 K fragment of phase A: key block i & 1, 64-dim step i >> 1 (32
-// bytes from the lane's K row, LDS row pitch KROWB bytes).
+// i-th fp8 K fragment of phase A: key block i & 1, 64-dim step i >> 1: the
+// lane's 32 bytes of its K row (kr0: the row in key block 0, LDS row pitch
+// KROWB bytes), two 16-byte chunks at the byte offsets k8o[2 * step] and
+// k8o[2 * step + 1] within the row (swizzled rows place the chunks apart).
 template <int KROWB>
-__device__ __forceinline__ i32x8 kfrag8(const char* kr0, int i) {
-  const char* p = kr0 + (i & 1) * 32 * KROWB + (i >> 1) * 64;
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+__device__ __forceinline__ i32x8 kfrag8(const char* kr0, const int (&k8o)[4], int i) {
+  const char* p = kr0 + (i & 1) * 32 * KROWB;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(p + k8o[2 * (i >> 1)]);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(p + k8o[2 * (i >> 1) + 1]);
   i32x8 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
@@ -701,7 +703,10 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int BQ = NW * 32;              // query rows per workgroup
   constexpr int KROW = D + 8;              // padded LDS pitch of a bf16 K row (elements)
   // LDS pitch of a K row in bytes (FP8 rows: D bytes + a 16-byte pad)
-  constexpr int KROWB = Q8 ? D + 16 : KROW * 2;
+  // FP8 K rows at D = 128: 128 bytes, 16-byte chunks swizzled like V^T rows
+  // (vswz), no padding; at D = 64 padded by 16 bytes
+  constexpr bool K8SWZ = Q8 && D == 128;
+  constexpr int KROWB = Q8 ? (K8SWZ ? D : D + 16) : KROW * 2;
   // bf16 K at D = 128: unpadded rows in blocks (KTileDmaBlk); the same tile size
   constexpr bool KBLK = !Q8 && D == 128;
   static_assert(!KBLK || 16 * kKBlkPitch == kBlockK * KROW * 2, "the block layout keeps the tile size");
@@ -902,7 +907,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const BufRange rk{kg, Q8 ? (uint32_t)(a.npad * D) : (uint32_t)(N - 1) * k_sn_bytes + D * 2};
   const BufRange rv{vg, (uint32_t)(D * a.npad * 2)};
   static_assert(KTILE * 2 % 1024 == 0 && VTILE * 2 % 1024 == 0, "tiles are whole 1-KB blocks");
-  using KDma = std::conditional_t<KBLK, KTileDmaBlk<NW>, TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW>>;
+  using KDma = std::conditional_t<KBLK, KTileDmaBlk<NW>, TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW, K8SWZ>>;
   using VDma = TileDma<VROW * 2, kBlockK / 8, VTILE * 2 / 1024, NW, VSWZ>;
   KDma kdma;
   VDma vdma;
@@ -965,7 +970,14 @@ void attn_bf16_kernel(AttnArgs a) {
   } else {
     kl[0] = kl[1] = krow_lane * KROW + hh * 8;
   }
-  const int koffb8 = krow_lane * KROWB + hh * 32;    // the same rows, FP8 bytes
+  const int koffb8 = krow_lane * KROWB;              // the same rows, FP8 bytes
+  // byte offsets in that row of the lane's chunks 4 * step + 2 * hh + half
+  int k8o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ch = 4 * (c >> 1) + 2 * hh + (c & 1);
+    k8o[c] = (K8SWZ ? ch ^ vswz(krow_lane) : ch) * 16;
+  }
   const int voff_lane = lq * VROW + (VSWZ ? 0 : hh * 8);   // phase B reads V^T rows db*32 + lq
   // element offsets of the lane's 16 bytes of 16-key chunk kc (keys 16*kc + 8*hh
   // .. +7) in its V^T row (swizzled: rows db*32 + lq share vswz, as 32 | db*32)
@@ -1005,7 +1017,7 @@ void attn_bf16_kernel(AttnArgs a) {
       const char* k8r = reinterpret_cast<const char*>(KBUF(0)) + koffb8;
       x[0] = x[1] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < NA; ++i) x[i & 1] = mfma_fp8(kfrag8<KROWB>(k8r, i), qf8[i >> 1], x[i & 1]);
+      for (int i = 0; i < NA; ++i) x[i & 1] = mfma_fp8(kfrag8<KROWB>(k8r, k8o, i), qf8[i >> 1], x[i & 1]);
     } else {
       qk_tile<D, KBS>(x, KBUF(0), kl, qf);
     }
@@ -1043,7 +1055,7 @@ void attn_bf16_kernel(AttnArgs a) {
     kmax_next = kmax_c[tile_at(1)];
     if (Q8) kscale_next = kscale_c[tile_at(1)];
     if constexpr (Q8) {
-      kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(1)) + koffb8, 0);
+      kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(1)) + koffb8, k8o, 0);
     } else {
       const __bf16* kr0 = KBUF(1);
       fr[0] = kfrag<KBS>(kr0, kl, 0);
@@ -1130,7 +1142,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         if (i + 1 < NA) {
-          kf8[(i + 1) & 1] = kfrag8<KROWB>(k8r, i + 1);
+          kf8[(i + 1) & 1] = kfrag8<KROWB>(k8r, k8o, i + 1);
         } else {
           fr[0] = vfrag<VROW, NDB>(vr0, vck, 0);
           fr[1] = vfrag<VROW, NDB>(vr0, vck, 1);
@@ -1214,7 +1226,7 @@ void attn_bf16_kernel(AttnArgs a) {
       const int j = i + 3;
       if (j < NB) fr[j & 3] = vfrag<VROW, NDB>(vr0, vck, j);
       else if (!Q8) fr[j & 3] = kfrag<KBS>(kn0, kl, j - NB);
-      else if (j == NB) kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(s2)) + koffb8, 0);
+      else if (j == NB) kf8[0] = kfrag8<KROWB>(reinterpret_cast<const char*>(KBUF(s2)) + koffb8, k8o, 0);
       const int db = i % NDB, kc = i / NDB;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i & 3], as_bf16x8(pw[kc]), o[db], 0, 0, 0);
       // spread 32 sums and 32 scale-FMAs over the fragments
