@@ -1,6 +1,6 @@
 """Throughput of TARA attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5|7]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5|7|8]
                     [--mode fused|partitioned|three-term|dense-bias|frame-loop] [--qk8]
 
 A step is one tara_attn_fwd call (metadata encoding, V layout pass, the fused
@@ -195,7 +195,7 @@ def oracle_configs(seconds: float):
         cores = max([int(i.get("num_threads", 0)) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
-    for cid in (1, 2, 3, 4, 5, 6, 7):
+    for cid in (1, 2, 3, 4, 5, 6, 7, 8):
         cfg = ti.config(cid)
         lay = cfg.layout()
         n, h, d = lay.n, cfg.heads, cfg.head_dim

@@ -211,12 +211,15 @@ _CONFIGS = {
     7: _cfg(5, "bf16-107682tok-56h-d128-chained2", 56, 128, "bf16", 107, (17, 29), (17, 29), 3, 556, 512,
             Params(window=0.10, falloff=0.40, strength=3.0, cap=8.0, binding=True,
                    gains=(1.25, 0.75, 0.75), chained=((0.8, 1.4, 1.1),)), mask=True, planes=2),
+    # the headline sequence at head dim 64 with twice the heads (the same model
+    # width H*D = 7,168 and the same attention FLOP)
+    8: _cfg(3, "bf16-107126tok-112h-d64", 112, 64, "bf16", 107, (17, 29), (17, 29), 2, 556, 512, Params()),
 }
 
 
 def config(cid: int) -> Config:
     """Workload by id (1..5; 6 = the 107,126-token layout at 56 heads; 7 = 5
-    with a second chained binding)."""
+    with a second chained binding; 8 = 6 at head dim 64 with 112 heads)."""
     return _CONFIGS[cid]
 
 

@@ -478,18 +478,23 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KEEP) : "memory");
 }
 
-// i-th K fragment of phase A: key block i & 1, head-dim step i >> 1, from the
-// K tile at kbuf. kl[kk & 1] is the lane's element offset for even / odd steps
-// kk (they differ in the block layout of KTileDmaBlk), KBS the element
-// distance between the two 32-row key blocks; step kk adds 16 elements.
-template <int KBS>
-__device__ __forceinline__ bf16x8 kfrag(const __bf16* kbuf, const int (&kl)[2], int i) {
-  return *reinterpret_cast<const bf16x8*>(kbuf + (i & 1) * KBS + kl[(i >> 1) & 1] + (i >> 1) * 16);
+// i-th K fragment of phase A: key block i & 1, head-dim step kk = i >> 1, from
+// the K tile at kbuf; KBS is the element distance between the two 32-row key
+// blocks. With two offsets, kl[kk & 1] is the lane's element offset for even /
+// odd steps (they differ in the block layout of KTileDmaBlk) and step kk adds
+// 16 elements; with one offset per step (swizzled 128-byte rows), kl[kk].
+template <int KBS, int NKL>
+__device__ __forceinline__ bf16x8 kfrag(const __bf16* kbuf, const int (&kl)[NKL], int i) {
+  const int kk = i >> 1;
+  int off;
+  if constexpr (NKL == 2) off = kl[kk & 1] + kk * 16;
+  else off = kl[kk];
+  return *reinterpret_cast<const bf16x8*>(kbuf + (i & 1) * KBS + off);
 }
 
 // S^T for the two 32-key blocks of a K tile in LDS.
-template <int D, int KBS>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const __bf16* kbuf, const int (&kl)[2],
+template <int D, int KBS, int NKL>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const __bf16* kbuf, const int (&kl)[NKL],
                                         const bf16x8 (&qf)[D / 16]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -701,7 +706,10 @@ void attn_bf16_kernel(AttnArgs a) {
   // of computing it
   static_assert(!DB || (PASS == PASS_FUSED && !Q8), "the dense-bias baseline is a fused bf16 pass");
   constexpr int BQ = NW * 32;              // query rows per workgroup
-  constexpr int KROW = D + 8;              // padded LDS pitch of a bf16 K row (elements)
+  // bf16 K rows at D = 64: 128 bytes, 16-byte chunks swizzled like V^T rows
+  // (vswz), no padding; at D = 128 see KBLK below
+  constexpr bool K64SWZ = !Q8 && D == 64;
+  constexpr int KROW = K64SWZ ? D : D + 8;  // LDS pitch of a bf16 K row (elements)
   // LDS pitch of a K row in bytes (FP8 rows: D bytes + a 16-byte pad)
   // FP8 K rows at D = 128: 128 bytes, 16-byte chunks swizzled like V^T rows
   // (vswz), no padding; at D = 64 padded by 16 bytes
@@ -907,7 +915,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const BufRange rk{kg, Q8 ? (uint32_t)(a.npad * D) : (uint32_t)(N - 1) * k_sn_bytes + D * 2};
   const BufRange rv{vg, (uint32_t)(D * a.npad * 2)};
   static_assert(KTILE * 2 % 1024 == 0 && VTILE * 2 % 1024 == 0, "tiles are whole 1-KB blocks");
-  using KDma = std::conditional_t<KBLK, KTileDmaBlk<NW>, TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW, K8SWZ>>;
+  using KDma = std::conditional_t<KBLK, KTileDmaBlk<NW>, TileDma<KROWB, Q8 ? D / 16 : D / 8, KTILE * 2 / 1024, NW, K8SWZ || K64SWZ>>;
   using VDma = TileDma<VROW * 2, kBlockK / 8, VTILE * 2 / 1024, NW, VSWZ>;
   KDma kdma;
   VDma vdma;
@@ -960,9 +968,14 @@ void attn_bf16_kernel(AttnArgs a) {
   i32x8 kf8[2];
   // phase A reads K rows kb*32 + perm32(lq): the lane's element offsets for even
   // and odd head-dim steps (equal unless KBLK: there row r's chunk 2*kk + hh sits
-  // at position (2*kk + hh) ^ (r & 3), 16 elements later or earlier)
-  int kl[2];
-  if (KBLK) {
+  // at position (2*kk + hh) ^ (r & 3), 16 elements later or earlier); with
+  // K64SWZ one offset per step kk, chunk 2*kk + hh of row r at (2*kk + hh) ^ vswz(r)
+  constexpr int NKL = K64SWZ ? NKK : 2;
+  int kl[NKL];
+  if constexpr (K64SWZ) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) kl[kk] = krow_lane * KROW + ((2 * kk + hh) ^ vswz(krow_lane)) * 8;
+  } else if constexpr (KBLK) {
     const int i_in = krow_lane & 3, b1 = i_in >> 1;
     const int base = (krow_lane >> 2) * (kKBlkPitch / 2) + i_in * D + 8 * (hh ^ (i_in & 1));
     kl[0] = base + 16 * b1;

@@ -41,7 +41,7 @@ def _head_rows(lay, seed, count=64):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 8])
 def test_fullsize_sampled_rows(cid):
     """One fused call over all heads; about 730 stratified rows of three heads
     and 64 stratified rows of every head against the oracle."""
