@@ -2,7 +2,8 @@
 benchmark times (all heads, one fused call; partitioned for the binding
 workload too), against the fp64 oracle: stratified samples of query rows on
 three heads, 64 stratified rows on every head, and one head each of the
-benchmark workload and of the binding workload on all rows. The outputs are NaN-poisoned before each call
+benchmark workload, of the binding workload and of the head-dim-64 workload on
+all rows. The outputs are NaN-poisoned before each call
 and every element of them must be written. Full-scale Q = 0 probes make the
 attention weights a function of the bias alone, so per-segment attention mass
 checks the temporal and binding terms at full size with a tight gate.
@@ -72,13 +73,14 @@ def test_fullsize_sampled_rows(cid):
             what=f"config {cid} fused, 64 rows on every one of {cfg.heads} heads")
 
 
-@pytest.mark.parametrize("cid,h", [(6, 27), (5, 41)])
+@pytest.mark.parametrize("cid,h", [(6, 27), (5, 41), (8, 90)])
 def test_fullsize_all_rows_one_head(cid, h):
     """One fused call with poisoned outputs, one head compared with the oracle
-    on every row (about 6e12 fp64 FLOP on the host each): the benchmark
-    workload 6 (107,126 tokens x 56 heads, d128) at head 27, and the binding
+    on every row (3e12 to 6e12 fp64 FLOP on the host each): the benchmark
+    workload 6 (107,126 tokens x 56 heads, d128) at head 27, the binding
     workload 5 (107,682 tokens x 56 heads, three pictures, a soft mask) at
-    head 41."""
+    head 41, and workload 8 (the benchmark sequence at 112 heads, d64) at
+    head 90."""
     cfg = ti.config(cid)
     lay = cfg.layout()
     q, k, v = ti.qkv(cfg)
