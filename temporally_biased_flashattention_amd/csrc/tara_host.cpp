@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <numeric>
 #include <string>
 #include <utility>
 #include <vector>
@@ -50,6 +51,56 @@ bool has_partials(const tara_params_t* p) {
   return p->mode == TARA_MODE_PARTITIONED || p->mode == TARA_MODE_THREE_TERM;
 }
 
+// Fused bf16 calls whose workgroups would leave the chip's last round of
+// compute units partly filled: the first m query blocks of every (batch, head)
+// run as the fused pass and fill whole rounds; the remaining ones run as the
+// range pass over `parts` key ranges (parts times as many workgroups, each over
+// 1/parts of the keys) followed by the exact LSE merge of those rows. Planned
+// for kTargetCUs compute units (MI355X) from the call shape alone, so that
+// tara_workspace_bytes and the call agree; the results are the same up to
+// rounding either way.
+constexpr int kTargetCUs = 256;
+constexpr int kMaxTailParts = 16;
+struct TailSplit {
+  int m = 0;       // query blocks per (batch, head) in the fused pass
+  int parts = 0;   // key ranges of the rest (0: no split)
+  int row0 = 0;    // first row of the rest
+};
+TailSplit tail_split(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
+  TailSplit t;
+  if (dtype != TARA_BF16 || p->mode != TARA_MODE_FUSED || p->qk8 || B <= 0 || H <= 0 || N <= 0) return t;
+  const int64_t bq = tara::attn_bf16_block_q(D), bh = (int64_t)B * H, nqb = (N + bq - 1) / bq;
+  const int64_t total = bh * nqb;
+  if (total <= kTargetCUs) return t;   // within one round: left as it is
+  // m: the most query blocks per (batch, head) whose workgroups fill whole rounds
+  const int64_t g = kTargetCUs / std::gcd(bh, (int64_t)kTargetCUs);
+  const int64_t m = nqb / g * g;
+  if (m == 0 || m == nqb) return t;
+  // rounds of one full-length workgroup per compute unit: ceil(total / CUs)
+  // unsplit; m's rounds plus the range pass's (its workgroups 1/parts as long)
+  const double unsplit = std::ceil((double)total / kTargetCUs);
+  const double main_rounds = (double)(bh * m / kTargetCUs);
+  const int64_t rest = bh * (nqb - m);
+  // only a partly filled last round is split, into at most two rounds of
+  // range-pass workgroups: the partial outputs stay small (at most 512 query
+  // blocks of fp32 O and LSE)
+  if (rest > kTargetCUs) return t;
+  double best = unsplit;
+  int best_parts = 0;
+  for (int pp = 2; pp <= kMaxTailParts && rest * pp <= 2 * kTargetCUs; ++pp) {
+    const double r = main_rounds + std::ceil((double)(rest * pp) / kTargetCUs) / pp;
+    if (r < best - 1e-9) {
+      best = r;
+      best_parts = pp;
+    }
+  }
+  if (best_parts == 0 || unsplit - best < 0.05) return t;   // too little to gain against the extra launches
+  t.m = (int)m;
+  t.parts = best_parts;
+  t.row0 = (int)(m * bq);
+  return t;
+}
+
 // 8-bit Q.K: the bf16 path in fused mode only
 bool uses_qk8(tara_dtype_t dtype, const tara_params_t* p) { return p->qk8 && dtype == TARA_BF16; }
 bool qk8_supported(tara_dtype_t dtype, const tara_params_t* p) {
@@ -64,8 +115,9 @@ int table_pictures(const tara_params_t* p) { return p->binding_enabled ? p->num_
 // Workspace regions, each 256-byte aligned: per-token encodings (with
 // binding, the per-query gain table), key-tile summaries, V^T (bf16 path),
 // the FP8 copy of K and its tile scales (8-bit Q.K), and per-partition O/LSE
-// (every mode but fused).
-WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
+// (every mode but fused; in fused mode those of the rows a tail split hands
+// to the range pass).
+WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p, const TailSplit& t) {
   WsLayout L{};
   const size_t npad = (size_t)npad_of(N), nkt = npad / tara::kBlockK;
   size_t off = 0;
@@ -92,6 +144,12 @@ WsLayout ws_layout_for(tara_dtype_t dtype, int B, int H, int N, int D, const tar
     const size_t parts = (size_t)num_parts(p);
     L.opart = take(parts * B * H * N * D * 4);
     L.lsepart = take(parts * B * H * N * 4);
+  } else {
+    if (t.parts) {   // the partial outputs of the split-off rows only
+      const size_t rows = (size_t)(N - t.row0);
+      L.opart = take((size_t)t.parts * B * H * rows * D * 4);
+      L.lsepart = take((size_t)t.parts * B * H * rows * 4);
+    }
   }
   L.total = off;
   return L;
@@ -235,6 +293,10 @@ int make_call(Call& c, const void* q, const void* k, const void* v, void* o, flo
   c.H = H;
   c.N = N;
   c.D = D;
+  const TailSplit t = tail_split(dtype, B, H, N, D, p);
+  c.tail_m = t.m;
+  c.tail_parts = t.parts;
+  c.tail_row0 = t.row0;
   if (B == 0 || H == 0 || N == 0) return TARA_OK;
   if (!q || !k || !v || !o || !lse) return fail(TARA_ERR_NULL_POINTER, "q, k, v, o and lse must be non-NULL");
   if (!seg_type || !token_time) return fail(TARA_ERR_NULL_POINTER, "seg_type and token_time must be non-NULL");
@@ -276,7 +338,15 @@ int make_call(Call& c, const void* q, const void* k, const void* v, void* o, flo
   return TARA_OK;
 }
 
-size_t call_workspace(const Call& c) { return ws_layout_for(c.dtype, c.B, c.H, c.N, c.D, c.p).total; }
+TailSplit call_tail(const Call& c) {
+  TailSplit t;
+  t.m = c.tail_m;
+  t.parts = c.tail_parts;
+  t.row0 = c.tail_row0;
+  return t;
+}
+
+size_t call_workspace(const Call& c) { return ws_layout_for(c.dtype, c.B, c.H, c.N, c.D, c.p, call_tail(c)).total; }
 
 Call sub_call(const Call& c, int b, int h0, int hc) {
   Call s = c;
@@ -310,7 +380,8 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
   const float* token_time = c.time;
   const int16_t* picture_id = c.pic;
   const float* mask_weight = c.mask;
-  const WsLayout L = ws_layout_for(dtype, B, H, N, D, p);
+  const TailSplit tail = call_tail(c);
+  const WsLayout L = ws_layout_for(dtype, B, H, N, D, p, tail);
 
   // derived constants, in double then rounded once to fp32
   const double log2e = 1.4426950408889634;
@@ -361,8 +432,10 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
   aa.o = o;
   aa.lse = lse;
   // per-partition outputs: every mode but fused (range partitions, the three terms)
-  aa.opart = has_partials(p) ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
-  aa.lsepart = has_partials(p) ? reinterpret_cast<float*>(ws + L.lsepart) : nullptr;
+  aa.opart = has_partials(p) || tail.parts ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
+  aa.lsepart = has_partials(p) || tail.parts ? reinterpret_cast<float*>(ws + L.lsepart) : nullptr;
+  aa.prow0 = 0;
+  aa.prows = N;
   aa.B = B;
   aa.H = H;
   aa.N = N;
@@ -410,7 +483,8 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
       if (r1 > r0) qranges.emplace_back(r0, r1);
     }
   } else {
-    qranges.emplace_back(0, N);
+    // a fused call with a tail split: the fused pass over the first rows only
+    qranges.emplace_back(0, tail.parts ? tail.row0 : N);
   }
   // passes of the attention kernel: one fused pass, one pass over all key
   // ranges, or the three terms
@@ -485,6 +559,35 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
     }
     if (e != hipSuccess) break;
   }
+  if (e == hipSuccess && tail.parts) {
+    // the split-off rows [row0, N): the range pass over `parts` tile-aligned
+    // key ranges, then their exact merge (inside the timed region: it is part
+    // of the attention work)
+    aa.qr0 = tail.row0;
+    aa.qr1 = N;
+    aa.nqb = (N - tail.row0 + block_q - 1) / block_q;
+    aa.nparts = tail.parts;
+    for (int i = 0; i <= tail.parts; ++i)
+      aa.kr[i] = i == tail.parts ? N : (int)std::min<int64_t>(N, (int64_t)nkt * i / tail.parts * kBlockK);
+    aa.prow0 = tail.row0;
+    aa.prows = N - tail.row0;
+    grid += attn_bf16_grid(aa) * tail.parts;
+    e = launch_attn_bf16(aa, D, PASS_RANGE, ATTN_PLAIN, stream);
+    ++launches;
+    if (e == hipSuccess) {
+      MergeArgs mg{};
+      mg.opart = aa.opart;
+      mg.lsepart = aa.lsepart;
+      mg.o = o;
+      mg.lse = lse;
+      mg.o_sb = o_str[0]; mg.o_sh = o_str[1]; mg.o_sn = o_str[2];
+      mg.B = B; mg.H = H; mg.N = N; mg.D = D; mg.nparts = tail.parts;
+      mg.row0 = tail.row0;
+      mg.rows = N - tail.row0;
+      e = launch_merge(mg, true, stream);
+      ++launches;
+    }
+  }
   if (ev1) {
     std::lock_guard<std::mutex> lk(g_tmu);
     (void)hipEventRecord(ev1, stream);
@@ -499,6 +602,8 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
     mg.lse = lse;
     mg.o_sb = o_str[0]; mg.o_sh = o_str[1]; mg.o_sn = o_str[2];
     mg.B = B; mg.H = H; mg.N = N; mg.D = D; mg.nparts = parts;
+    mg.row0 = 0;
+    mg.rows = N;
     e = launch_merge(mg, dtype == TARA_BF16, stream);
     ++launches;
     if (e != hipSuccess) return fail(TARA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
@@ -585,7 +690,7 @@ size_t tara_workspace_bytes(int dtype_, int B, int H, int N, int D, const tara_p
   if (!qk8_supported(dtype, p)) return (size_t)-1;
   if (p->mode == TARA_MODE_DENSE_BIAS && dtype != TARA_BF16) return (size_t)-1;
   if (B == 0 || H == 0 || N == 0) return 0;
-  return ws_layout_for(dtype, B, H, N, D, p).total;
+  return ws_layout_for(dtype, B, H, N, D, p, tail_split(dtype, B, H, N, D, p)).total;
 }
 
 const char* tara_status_string(int status) {

@@ -90,8 +90,10 @@ struct AttnArgs {
   int64_t o_sb, o_sh, o_sn;
   void* o;                 // fused: final O (input dtype)
   float* lse;              // fused: final LSE [B][H][N]
-  float* opart;            // partitioned: O_p fp32 [P][B][H][N][D]
-  float* lsepart;          // partitioned: LSE_p [P][B][H][N]
+  float* opart;            // partitioned: O_p fp32 [P][B][H][prows][D]
+  float* lsepart;          // partitioned: LSE_p [P][B][H][prows]
+  int prow0, prows;        // rows [prow0, prow0 + prows) of each (b, h) that O_p / LSE_p hold
+                           // (their N above is prows; 0 and N but for the fused pass's tail)
   int B, H, N, npad, nkt, nqb;
   int qr0, qr1;            // query rows of this launch: [qr0, qr1) (all: 0, N); nqb covers them
   const float* tq;
@@ -123,6 +125,7 @@ struct MergeArgs {
   float* lse;
   int64_t o_sb, o_sh, o_sn;
   int B, H, N, D, nparts;
+  int row0, rows;          // merge rows [row0, row0 + rows) of each (b, h); partials hold rows - row0
 };
 
 hipError_t launch_meta(const MetaArgs& a, hipStream_t s);
@@ -165,6 +168,11 @@ struct Call {
   const float* mask;
   int64_t mask_plane;
   const tara_params_t* p;
+  // a fused call's tail split, planned for the whole call (B, H) and kept by
+  // its sub-calls, so that they run the same passes per head: query blocks
+  // per (b, h) in the fused pass, key ranges of the rest (0: none), first row
+  // of the rest
+  int tail_m, tail_parts, tail_row0;
 };
 // Checks the arguments of tara_attn_fwd (everything but the workspace) and
 // fills c; a nonzero status (with the thread's last error set) on failure.

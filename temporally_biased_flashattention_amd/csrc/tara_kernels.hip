@@ -817,12 +817,12 @@ void attn_bf16_kernel(AttnArgs a) {
   // an empty partition contributes nothing to the merge
   auto write_empty = [&]() {
     if (PART && qvalid) {
-      float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
+      float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * a.prows + (qrow - a.prow0)) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = f32x4{};
-      if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = -INFINITY;
+      if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * a.prows + (qrow - a.prow0)] = -INFINITY;
     }
   };
   if (k1 <= k0) {
@@ -1292,7 +1292,7 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   }
   if (PART) {
-    float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D;
+    float* op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * a.prows + (qrow - a.prow0)) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1302,7 +1302,7 @@ void attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) y[i] = o[db][j * 4 + i] * inv;
         *reinterpret_cast<f32x4*>(op + db * 32 + j * 8 + hh * 4) = y;
       }
-    if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = lse;
+    if (hh == 0) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * a.prows + (qrow - a.prow0)] = lse;
   } else {
     __bf16* op = static_cast<__bf16*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qrow * a.o_sn;
 #pragma unroll
@@ -1531,13 +1531,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const float inv = empty ? 0.0f : 1.0f / l;
   const float lse = empty ? -INFINITY : (m + log2f(l)) * kLn2;
   float* op;
-  if (PART) op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * N + qrow) * D + sub * DL;
+  if (PART) op = a.opart + ((((int64_t)part * a.B + b) * a.H + h) * a.prows + (qrow - a.prow0)) * D + sub * DL;
   else op = static_cast<float*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qrow * a.o_sn + sub * DL;
 #pragma unroll
   for (int i = 0; i < DL; i += 4)
     *reinterpret_cast<f32x4*>(op + i) = f32x4{ov[i] * inv, ov[i + 1] * inv, ov[i + 2] * inv, ov[i + 3] * inv};
   if (sub == 0) {
-    if (PART) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * N + qrow] = lse;
+    if (PART) a.lsepart[(((int64_t)part * a.B + b) * a.H + h) * a.prows + (qrow - a.prow0)] = lse;
     else a.lse[((int64_t)b * a.H + h) * N + qrow] = lse;
   }
 }
@@ -1572,12 +1572,12 @@ template <bool BF16_OUT, int NP>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int dq = a.D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const int64_t rows = (int64_t)a.B * a.H * a.rows;
   if (gid >= rows * dq) return;
   const int d8 = (int)(gid % dq);
-  const int64_t row = gid / dq;                   // (b*H + h)*N + n
-  const int n = (int)(row % a.N);
-  const int64_t bh = row / a.N;
+  const int64_t row = gid / dq;                   // (b*H + h)*rows + n - row0: the partials' row
+  const int n = a.row0 + (int)(row % a.rows);
+  const int64_t bh = row / a.rows;
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
   const int np = NP > 0 ? NP : a.nparts;
   f32x4 acc0 = f32x4{}, acc1 = f32x4{};
@@ -1636,7 +1636,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     *reinterpret_cast<f32x4*>(o) = acc0;
     *reinterpret_cast<f32x4*>(o + 4) = acc1;
   }
-  if (d8 == 0) a.lse[row] = lse;
+  if (d8 == 0) a.lse[bh * a.N + n] = lse;
 }
 
 template <bool BF16_OUT>
@@ -1648,7 +1648,7 @@ void launch_merge_np(const MergeArgs& a, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool bf16_out, hipStream_t s) {
-  const int64_t total = (int64_t)a.B * a.H * a.N * (a.D / 8);
+  const int64_t total = (int64_t)a.B * a.H * a.rows * (a.D / 8);
   dim3 grid((unsigned)((total + 255) / 256));
   if (bf16_out) launch_merge_np<true>(a, grid, s);
   else launch_merge_np<false>(a, grid, s);

@@ -65,17 +65,13 @@ extern "C" int tara_attn_fwd_noalloc(const void* q, const void* k, const void* v
     tara::set_empty_info(c);
     return TARA_OK;
   }
-  // the largest group of heads whose workspace fits (it grows with the head count)
+  // the largest group of heads whose workspace fits, for a full group and for
+  // the last, smaller one (the workspace need not grow with the head count: a
+  // fused call's tail split depends on it)
+  auto fits = [&](int heads) { return tara::call_workspace(tara::sub_call(c, 0, 0, heads)) <= kScratchBytes; };
   int hc = 0;
-  for (int lo = 1, hi = H; lo <= hi;) {
-    const int mid = lo + (hi - lo) / 2;
-    if (tara::call_workspace(tara::sub_call(c, 0, 0, mid)) <= kScratchBytes) {
-      hc = mid;
-      lo = mid + 1;
-    } else {
-      hi = mid - 1;
-    }
-  }
+  for (int g = H; g >= 1 && hc == 0; --g)
+    if (fits(g) && (H % g == 0 || fits(H % g))) hc = g;
   if (hc == 0)
     return tara::set_error(TARA_ERR_WORKSPACE,
                            "the no-alloc entry point holds " + std::to_string(kScratchBytes) +
@@ -89,6 +85,8 @@ extern "C" int tara_attn_fwd_noalloc(const void* q, const void* k, const void* v
     for (int h0 = 0; h0 < H; h0 += hc) {
       // the first group of a batch element encodes its metadata; the others reuse it
       const tara::Call s = tara::sub_call(c, b, h0, std::min(hc, H - h0));
+      if (tara::call_workspace(s) > kScratchBytes)   // guarded by the choice of hc above
+        return tara::set_error(TARA_ERR_WORKSPACE, "internal: a group of heads outgrew the no-alloc array");
       if (int st = tara::enqueue_call(s, static_cast<char*>(ws), h0 == 0, false, stream, &sub)) return st;
       const int grid = info.grid + sub.grid, launches = info.launches + sub.launches;
       info = sub;

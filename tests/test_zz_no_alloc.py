@@ -6,8 +6,9 @@ its outputs must equal the workspace entry point's exactly. Two calls in a
 row, the second smaller: the benchmark's 107,126-token sequence at 9 heads
 (three groups of heads through the array), then a small two-element batch
 with two chained bindings (each batch element reads its own rows of both mask
-planes). Then the partitioned and three-term modes, and the rejection of a
-call whose single head needs more than the array holds.
+planes). A fused call with a tail split run in groups of heads. Then the
+partitioned and three-term modes, and the rejection of a call whose single
+head needs more than the array holds.
 """
 import numpy as np
 import pytest
@@ -75,6 +76,21 @@ def test_noalloc_matches_two_calls_second_smaller():
     tgt = torch.from_numpy(lay2.seg == 0).float()
     mask = (torch.rand(2, 2, lay2.n, generator=g) * tgt).cuda()
     _same(*_both(q, k, v, lay2, CHAIN, 2, mask=mask)[:2], f"B=2 x 3 heads x {lay2.n} tokens, chained bindings")
+
+
+def test_noalloc_tail_split_in_groups():
+    """107,126 tokens x 8 heads x d128: the fused call hands each head's last
+    630 rows to the range pass over ten key ranges (its workgroups would leave
+    the last round of compute units nearly empty). The call needs more than the
+    array, so the no-alloc entry point runs it in groups of heads; every group
+    keeps the call's split, and the outputs equal the workspace entry point's."""
+    lay = ti.config(6).layout()
+    g = torch.Generator().manual_seed(5105)
+    q, k, v = (torch.randn(1, 8, lay.n, 128, generator=g).to(torch.bfloat16).cuda() for _ in range(3))
+    a, b, info = _both(q, k, v, lay, ti.Params(), 1)
+    log(f"no-alloc run info: {info}")
+    assert info["grid"] == 8 * 416 + 8 * 3 * 10, info
+    _same(a, b, "107,126 tokens x 8 heads, tail split")
 
 
 @pytest.mark.parametrize("mode", ["partitioned", "three-term", "frame-loop"])
