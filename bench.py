@@ -366,7 +366,10 @@ def main():
                                 "strength": cfg.params.strength, "cap": cfg.params.cap,
                                 "binding": cfg.params.binding, "gains": list(cfg.params.gains),
                                 "chained_gains": [list(c) for c in cfg.params.chained]},
-                   "block_q": info.get("block_q"), "block_k": info.get("block_k"), "grid": info.get("grid")},
+                   "block_q": info.get("block_q"), "block_k": info.get("block_k"), "grid": info.get("grid"),
+                   # fused bf16: the last query blocks of every head run as a range pass over this many
+                   # key ranges plus a merge (0: none); the timed attention work includes both
+                   "tail_parts": info.get("tail_parts")},
         "roofline": {"bound": "alu" if fp32_path else "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",

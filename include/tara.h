@@ -282,11 +282,13 @@ typedef struct {
   int num_partitions;    /* 1 in fused mode; query ranges in FRAME_LOOP mode */
   int block_q;           /* query rows per workgroup of the attention kernel */
   int block_k;           /* keys per tile */
-  int grid;              /* workgroups of the attention kernel (all partitions) */
+  int grid;              /* workgroups of the attention kernel (all partitions and passes) */
   int launches;          /* kernels enqueued by the call (the debug kernel not counted) */
   int elem_all;          /* 1 when TARA_DISABLE_TILE_SKIP=1 sent every tile down the per-element path */
   int tile_stats;        /* 1 when the counts below were taken */
-  int reserved;
+  int tail_parts;        /* fused bf16: key ranges of the range pass that took the last query blocks
+                            of every (batch, head) (their workgroups would have left the last round
+                            of compute units partly filled); 0 when the fused pass took all rows */
   long long tiles_plain, tiles_saturated, tiles_window, tiles_picture, tiles_elem;
 } tara_run_info_t;
 

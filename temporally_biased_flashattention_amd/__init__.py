@@ -85,7 +85,7 @@ class TaraParams(ctypes.Structure):
 class TaraRunInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "mode", "dtype", "bias_active", "binding_active", "num_partitions",
-        "block_q", "block_k", "grid", "launches", "elem_all", "tile_stats", "reserved")] + [
+        "block_q", "block_k", "grid", "launches", "elem_all", "tile_stats", "tail_parts")] + [
         (n, ctypes.c_longlong) for n in (
             "tiles_plain", "tiles_saturated", "tiles_window", "tiles_picture", "tiles_elem")]
 

@@ -620,6 +620,7 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
   info.grid = grid;
   info.launches = launches;
   info.elem_all = aa.elem_all;
+  info.tail_parts = tail.parts;
   const bool log = env_flag("TARA_LOG");
   if (debug && (log || env_flag("TARA_TILE_STATS")) && dtype == TARA_BF16 &&
       (p->mode == TARA_MODE_FUSED || p->mode == TARA_MODE_PARTITIONED)) {
@@ -654,6 +655,8 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
     if (info.tile_stats)
       std::fprintf(stderr, " tiles plain=%lld saturated=%lld window=%lld picture=%lld elem=%lld",
                    info.tiles_plain, info.tiles_saturated, info.tiles_window, info.tiles_picture, info.tiles_elem);
+    if (tail.parts)
+      std::fprintf(stderr, " tail: rows %d.. over %d key ranges", tail.row0, tail.parts);
     std::fprintf(stderr, "\n");
   }
   return TARA_OK;

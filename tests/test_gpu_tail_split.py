@@ -52,7 +52,7 @@ def test_tail_split_rows(d, B):
     info = tara.tara_get_last_run_info()
     log(f"D={d} B={B}: run info {info}")
     # meta, V^T, key norms, the fused pass, the range pass over the split-off rows, their merge
-    assert info["launches"] == 6
+    assert info["launches"] == 6 and info["tail_parts"] == 2
     assert info["grid"] == B * H * 64 + B * H * 15 * 2
     ro, rl = run_oracle(q, k, v, lay, p, rows=rows)
     compare(o.numpy(), l.numpy(), ro, rl, what=f"tail split D={d}, B={B}, {len(rows)} rows x {H} heads")
