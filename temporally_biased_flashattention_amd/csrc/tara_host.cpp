@@ -51,7 +51,7 @@ bool has_partials(const tara_params_t* p) {
   return p->mode == TARA_MODE_PARTITIONED || p->mode == TARA_MODE_THREE_TERM;
 }
 
-// Fused bf16 calls whose workgroups would leave the chip's last round of
+// Fused bf16 calls (8-bit Q.K too) whose workgroups would leave the last round of
 // compute units partly filled: the first m query blocks of every (batch, head)
 // run as the fused pass and fill whole rounds; the remaining ones run as the
 // range pass over `parts` key ranges (parts times as many workgroups, each over
@@ -68,7 +68,7 @@ struct TailSplit {
 };
 TailSplit tail_split(tara_dtype_t dtype, int B, int H, int N, int D, const tara_params_t* p) {
   TailSplit t;
-  if (dtype != TARA_BF16 || p->mode != TARA_MODE_FUSED || p->qk8 || B <= 0 || H <= 0 || N <= 0) return t;
+  if (dtype != TARA_BF16 || p->mode != TARA_MODE_FUSED || B <= 0 || H <= 0 || N <= 0) return t;
   const int64_t bq = tara::attn_bf16_block_q(D), bh = (int64_t)B * H, nqb = (N + bq - 1) / bq;
   const int64_t total = bh * nqb;
   if (total <= kTargetCUs) return t;   // within one round: left as it is
@@ -572,7 +572,7 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
     aa.prow0 = tail.row0;
     aa.prows = N - tail.row0;
     grid += attn_bf16_grid(aa) * tail.parts;
-    e = launch_attn_bf16(aa, D, PASS_RANGE, ATTN_PLAIN, stream);
+    e = launch_attn_bf16(aa, D, PASS_RANGE, variant, stream);
     ++launches;
     if (e == hipSuccess) {
       MergeArgs mg{};

@@ -701,7 +701,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)
 void attn_bf16_kernel(AttnArgs a) {
   constexpr bool PART = PASS != PASS_FUSED;   // writes one partition's (O_p, LSE_p)
   constexpr bool TERM = PASS >= PASS_TERM_A;  // visits a listed subset of the key tiles
-  static_assert(!Q8 || PASS == PASS_FUSED, "8-bit Q.K is built for the fused pass");
+  static_assert(!Q8 || PASS == PASS_FUSED || PASS == PASS_RANGE,
+                "8-bit Q.K is built for the fused pass and the range pass of a fused call's tail");
   // DB: the dense-bias baseline reads every logit's bias from a.dbias instead
   // of computing it
   static_assert(!DB || (PASS == PASS_FUSED && !Q8), "the dense-bias baseline is a fused bf16 pass");
@@ -1392,7 +1393,10 @@ void launch_attn_bf16_d(const AttnArgs& a, int pass, int variant, dim3 grid, dim
         hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_FUSED, false, false>), grid, block, 0, s, a);
       break;
     case PASS_RANGE:
-      hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE, false, false>), grid, block, 0, s, a);
+      if (variant == ATTN_QK8)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE, true, false>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_RANGE, false, false>), grid, block, 0, s, a);
       break;
     case PASS_TERM_A:
       hipLaunchKernelGGL((attn_bf16_kernel<D, kWaves, PASS_TERM_A, false, false>), grid, block, 0, s, a);
@@ -1407,9 +1411,10 @@ void launch_attn_bf16_d(const AttnArgs& a, int pass, int variant, dim3 grid, dim
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int D, int pass, int variant, hipStream_t s) {
-  // 8-bit Q.K and the dense-bias baseline exist for the one-pass form only
-  // (the host rejects the rest)
-  if (variant != ATTN_PLAIN && pass != PASS_FUSED) return hipErrorInvalidValue;
+  // the dense-bias baseline exists for the one-pass form only, 8-bit Q.K for
+  // it and the range pass of a fused call's tail (the host rejects the rest)
+  if (variant == ATTN_DENSE_BIAS && pass != PASS_FUSED) return hipErrorInvalidValue;
+  if (variant == ATTN_QK8 && pass != PASS_FUSED && pass != PASS_RANGE) return hipErrorInvalidValue;
   dim3 grid(attn_bf16_grid(a), pass == PASS_RANGE ? a.nparts : 1);
   dim3 block(kWaves * 64);
   if (D == 128) launch_attn_bf16_d<128>(a, pass, variant, grid, block, s);

@@ -249,8 +249,9 @@ def test_timing_read_empty(lib):
 def test_workspace_bytes_tail_split():
     """A fused bf16 call of 20,020 tokens x 8 heads (79 query blocks of 256
     rows per head: 632 workgroups, 2.5 rounds of 256 compute units) hands rows
-    16,384.. to the range pass over two key ranges: the workspace holds their
-    partial O and LSE. Other modes, fp32 and calls within one round do not."""
+    16,384.. to the range pass over two key ranges (with 8-bit Q.K too): the
+    workspace holds their partial O and LSE. Other modes, fp32 and calls
+    within one round do not."""
     p = tara.tara_params_default()
     B, H, N, D = 1, 8, 20020, 128
     npad = (N + 63) // 64 * 64
@@ -262,6 +263,6 @@ def test_workspace_bytes_tail_split():
     tail = _al(2 * B * H * rows * D * 4) + _al(2 * B * H * rows * 4)
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, p) == base + tail
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, H, N, D, tara.make_params(qk8=True)) == (
-        base + _al(B * H * npad * D) + _al(B * H * nkt * 4))
+        base + _al(B * H * npad * D) + _al(B * H * nkt * 4) + tail)
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, 1, 2000, D, p) == tara.tara_workspace_bytes(
         tara.TARA_BF16, B, 1, 2000, D, tara.make_params(mode="frame-loop", partitions=1))

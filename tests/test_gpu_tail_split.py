@@ -71,3 +71,23 @@ def test_no_split_below_one_round():
     q, k, v = qkv_random(1, 8, lay.n, 128, seed=7800)
     run_gpu(q, k, v, lay, ti.Params(), rows=np.arange(lay.n))
     assert tara.tara_get_last_run_info()["launches"] == 4
+
+
+def test_tail_split_qk8():
+    """8-bit Q.K: the range pass of the tail takes FP8 products too. Rows on
+    both sides of the split and the last rows against the oracle run on the
+    dequantised Q and K (the usual gates)."""
+    from tara_testlib import dequantized
+    lay = _layout()
+    n = lay.n
+    H, d = 8, 128
+    split_row = 64 * 256
+    q, k, v = qkv_random(1, H, n, d, seed=7900)
+    rows = np.unique(np.concatenate([np.arange(split_row - 24, split_row + 24), np.arange(n - 24, n)]))
+    o, l = run_gpu(q, k, v, lay, ti.Params(), qk8=True, rows=rows, poison=True)
+    info = tara.tara_get_last_run_info()
+    assert info["tail_parts"] == 2 and info["launches"] == 6, info
+    hs = list(range(H))
+    qd, kd = dequantized(q, k, heads=hs, rows=rows)
+    ro, rl = run_oracle(qd, kd, v, lay, ti.Params(), rows=rows, heads=hs)
+    compare(o.numpy(), l.numpy(), ro, rl, what=f"tail split 8-bit Q.K, {len(rows)} rows x {H} heads")
