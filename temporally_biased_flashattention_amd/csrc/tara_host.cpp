@@ -81,13 +81,13 @@ TailSplit tail_split(tara_dtype_t dtype, int B, int H, int N, int D, const tara_
   const double unsplit = std::ceil((double)total / kTargetCUs);
   const double main_rounds = (double)(bh * m / kTargetCUs);
   const int64_t rest = bh * (nqb - m);
-  // only a partly filled last round is split, into at most two rounds of
-  // range-pass workgroups: the partial outputs stay small (at most 512 query
-  // blocks of fp32 O and LSE)
-  if (rest > kTargetCUs) return t;
+  // at most two rounds of query blocks are split off, into at most four
+  // rounds of range-pass workgroups: the partial outputs stay small (at most
+  // 1,024 query blocks of fp32 O and LSE)
+  if (rest > 2 * kTargetCUs) return t;
   double best = unsplit;
   int best_parts = 0;
-  for (int pp = 2; pp <= kMaxTailParts && rest * pp <= 2 * kTargetCUs; ++pp) {
+  for (int pp = 2; pp <= kMaxTailParts && rest * pp <= 4 * kTargetCUs; ++pp) {
     const double r = main_rounds + std::ceil((double)(rest * pp) / kTargetCUs) / pp;
     if (r < best - 1e-9) {
       best = r;
