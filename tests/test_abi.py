@@ -266,3 +266,25 @@ def test_workspace_bytes_tail_split():
         base + _al(B * H * npad * D) + _al(B * H * nkt * 4) + tail)
     assert tara.tara_workspace_bytes(tara.TARA_BF16, B, 1, 2000, D, p) == tara.tara_workspace_bytes(
         tara.TARA_BF16, B, 1, 2000, D, tara.make_params(mode="frame-loop", partitions=1))
+
+
+def test_tail_split_plan_at_the_benchmark_shapes():
+    """The planned tail splits of the benchmark shapes, read off the workspace
+    (the partial O and LSE of the split-off rows): at 107,126 tokens x 56
+    heads, 3 of 419 query blocks per head (630 rows) in 3 key ranges; at 8
+    heads the same rows in 10 key ranges; at 112 heads x d64, 3 key ranges;
+    at 9 heads (1,467 blocks left over, more than two rounds) none."""
+    p = tara.tara_params_default()
+    N = 107126
+
+    def ws(H, D, params=p):
+        return tara.tara_workspace_bytes(tara.TARA_BF16, 1, H, N, D, params)
+
+    def partials(H, D, parts, rows=630):
+        return _al(parts * H * rows * D * 4) + _al(parts * H * rows * 4)
+
+    unsplit = tara.make_params(mode="frame-loop", partitions=1)   # same regions, never split
+    assert ws(56, 128) == ws(56, 128, unsplit) + partials(56, 128, 3)
+    assert ws(8, 128) == ws(8, 128, unsplit) + partials(8, 128, 10)
+    assert ws(112, 64) == ws(112, 64, unsplit) + partials(112, 64, 3)
+    assert ws(9, 128) == ws(9, 128, unsplit)
