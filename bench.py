@@ -372,7 +372,8 @@ def main():
                    "tail_parts": info.get("tail_parts")},
         "roofline": {"bound": "alu" if fp32_path else "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
+                     "kernel": ("attn_bf16_kernel" + (" (fused pass + tail range pass + merge)" if info.get("tail_parts") else ""))
+                               if cfg.dtype == "bf16" else "attn_f32_kernel",
                      "kernel_ms_avg": round(k_avg, 4), "launches_timed": len(kms),
                      "kernel_ms_median": round(sorted(kms)[len(kms) // 2], 4) if kms else None,
                      "kernel_ms_min": round(min(kms), 4) if kms else None,
