@@ -39,8 +39,9 @@ penalty and of Q = 0 attention, reduction to a library softmax attention
 when the bias is off, brute force on tiny inputs, the partition merge and
 three-term identities, invariances, monotonicity, chained bindings, and the
 8-bit rounding against the format's definition; planted mistakes must fail
-them. Absolute O and LSE on random inputs are pinned only through these: the
-pages print no attention outputs (parity unpinned beyond the pins).
+them. Every function here has such a pin. The pages print no attention
+outputs for a worked example, so absolute O and LSE on random inputs are pinned
+through these: the library reduction, brute force and the closed forms.
 """
 from __future__ import annotations
 
