@@ -116,6 +116,75 @@ def mask_blob(frames: int, rows: int, cols: int, seed: int = 5000, sub: int = 8)
     return out
 
 
+def shot_length_ok(frames: int) -> bool:
+    """True for a prepared shot length of 17n + 5 frames (n >= 0), padding
+    included: the only multi-frame mask length the binding page accepts
+    ("BFS H3 Reference Attention Binding (Experimental)", "Common issues")."""
+    return isinstance(frames, (int, np.integer)) and frames >= 5 and (frames - 5) % 17 == 0
+
+
+def _area_weights(src: int, dst: int) -> np.ndarray:
+    """[dst, src] weights of area resampling: output cell i covers the source
+    interval [i*src/dst, (i+1)*src/dst) and averages the source cells it
+    overlaps, each weighted by the length of the overlap. Rows sum to 1."""
+    e = np.arange(dst + 1, dtype=np.float64) * (src / dst)
+    p = np.arange(src, dtype=np.float64)
+    ov = np.minimum(e[1:, None], p[None, :] + 1.0) - np.maximum(e[:-1, None], p[None, :])
+    return np.clip(ov, 0.0, None) / (src / dst)
+
+
+def latent_spans(frames: int, latent_frames: int) -> List[tuple]:
+    """Pixel frames [lo, hi) averaged into each latent frame: the shot's
+    frames split into latent_frames consecutive spans of near-equal length
+    (each at least one frame; with one frame, every latent frame takes it)."""
+    spans = []
+    for j in range(latent_frames):
+        lo = j * frames // latent_frames
+        hi = max(lo + 1, (j + 1) * frames // latent_frames)
+        spans.append((min(lo, frames - 1), min(hi, frames)))
+    return spans
+
+
+def prepare_target_mask(mask, shot_frames: int, latent_frames: int, grid: tuple) -> np.ndarray:
+    """Mask weight m of every target token from a soft pixel-space mask.
+
+    mask: [F, height, width] (or [height, width], one static mask) with
+    F = 1 or F = shot_frames, the prepared shot length (17n + 5 frames at
+    24 fps, padding included); anything else raises ValueError, as a whole-clip
+    mask fed to one shot does on the binding page ("BFS H3 Reference Attention
+    Binding (Experimental)", "Common issues"). The mask marks output positions.
+
+    Each frame is area-downsampled to the target patch grid (rows, cols), then
+    the frames of each latent frame's span (latent_spans) are averaged (the
+    same page, "The exact rule": soft masks are area-downsampled to the target
+    patch resolution and averaged over the latent temporal spans). Returns
+    float32 [latent_frames * rows * cols] in the packed target order
+    (frame-major, patches row-major), the per-token mask of the C ABI.
+    """
+    if not shot_length_ok(shot_frames):
+        raise ValueError(f"shot length {shot_frames}: a prepared shot has 17n + 5 frames, padding included")
+    m = np.asarray(mask, dtype=np.float64)
+    if m.ndim == 2:
+        m = m[None]
+    if m.ndim != 3 or min(m.shape) < 1:
+        raise ValueError("mask must be [frames, height, width] or [height, width]")
+    frames = m.shape[0]
+    if frames not in (1, shot_frames):
+        raise ValueError(f"mask length {frames}: one frame or exactly the shot's {shot_frames} frames")
+    if not np.isfinite(m).all():
+        raise ValueError("mask values must be finite")
+    rows, cols = grid
+    if latent_frames < 1 or rows < 1 or cols < 1:
+        raise ValueError("latent_frames and the patch grid must be positive")
+    ar = _area_weights(m.shape[1], rows)
+    ac = _area_weights(m.shape[2], cols)
+    small = np.einsum("ip,fpq,jq->fij", ar, m, ac)   # [F, rows, cols]
+    out = np.empty((latent_frames, rows, cols), np.float64)
+    for j, (lo, hi) in enumerate(latent_spans(frames, latent_frames)):
+        out[j] = small[lo:hi].mean(axis=0)
+    return out.reshape(-1).astype(np.float32)
+
+
 def make_layout(frames: int, target_hw: tuple, guide_hw: tuple, pictures: int,
                 picture_tokens: int, text: int, mask: bool = False,
                 mask_seed: int = 5000, mask_planes: int = 1) -> Layout:
