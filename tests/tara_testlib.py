@@ -108,6 +108,36 @@ def run_oracle(q, k, v, lay: ti.Layout, p: ti.Params, rows=None, heads: Optional
     return o, lse
 
 
+def run_oracle_all_heads(q, k, v, lay: ti.Layout, p: ti.Params, workers: int = 8):
+    """run_oracle on every row of every head of batch element 0, one head per
+    job on `workers` threads of this process (NumPy releases the GIL inside its
+    array loops; BLAS shares the host's cores, at most 16, among them while
+    they run). No child process is started. Returns O [1, H, N, D], LSE [1, H, N]."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor, as_completed
+
+    from threadpoolctl import threadpool_limits
+
+    _, H, N, D = q.shape
+    workers = max(1, min(workers, H))
+    blas_threads = max(1, min(16, len(os.sched_getaffinity(0))) // workers)
+    pf = p.f32()
+    o = np.zeros((1, H, N, v.shape[-1]))
+    lse = np.zeros((1, H, N))
+
+    def job(h):
+        return h, oracle.attention_head(q[0, h].float().numpy(), k[0, h].float().numpy(), v[0, h].float().numpy(),
+                                        lay.seg, lay.time, lay.picture, lay.mask, pf)
+
+    with threadpool_limits(limits=blas_threads, user_api="blas"):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            for fut in as_completed([ex.submit(job, h) for h in range(H)]):
+                h, (oh, lh) = fut.result()
+                o[0, h], lse[0, h] = oh, lh
+                log(f"oracle head {h}: all {N} rows done")
+    return o, lse
+
+
 def compare(o_gpu, lse_gpu, o_ref, lse_ref, tol_o=TOL_O, tol_lse=TOL_LSE, tol_rel=TOL_REL_O, what=""):
     """Element-by-element comparison. tol_o is a number or an array of
     per-element bounds broadcastable to O."""

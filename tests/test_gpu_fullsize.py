@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (all heads, one fused call; partitioned for the binding
 workload too), against the fp64 oracle: stratified samples of query rows on
-three heads, 64 stratified rows on every head, and one head each of the
+three heads, 64 stratified rows on every head, every row of every head of
+the 54,272-token, 8-head workload, and one head each of the
 benchmark workload, of the binding workload and of the head-dim-64 workload on
 all rows. The outputs are NaN-poisoned before each call
 and every element of them must be written. Full-scale Q = 0 probes make the
@@ -13,7 +14,7 @@ import pytest
 import torch
 
 import tara_inputs as ti
-from tara_testlib import compare, log, run_gpu, run_oracle, sample_rows
+from tara_testlib import compare, log, run_gpu, run_oracle, run_oracle_all_heads, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +72,20 @@ def test_fullsize_sampled_rows(cid):
         ref_l.append(hl)
     compare(np.concatenate(go, 1), np.concatenate(gl, 1), np.concatenate(ref_o, 1), np.concatenate(ref_l, 1),
             what=f"config {cid} fused, 64 rows on every one of {cfg.heads} heads")
+
+
+def test_config2_all_rows_all_heads():
+    """Workload 2 (54,272 tokens x 8 heads, d128) in the launch configuration
+    the benchmark times for it (one fused call over all heads, the tail split
+    included), outputs NaN-poisoned, compared with the oracle on every row of
+    every head (1.2e13 fp64 FLOP on the host, one head per worker thread)."""
+    cfg = ti.config(2)
+    lay = cfg.layout()
+    q, k, v = ti.qkv(cfg)
+    o, l = run_gpu(q, k, v, lay, cfg.params, poison=True)
+    log(f"config 2: N={lay.n} H={cfg.heads}; oracle on all rows and heads")
+    ro, rl = run_oracle_all_heads(q, k, v, lay, cfg.params)
+    compare(o.numpy(), l.numpy(), ro, rl, what=f"config 2, all {lay.n} rows of all {cfg.heads} heads")
 
 
 @pytest.mark.parametrize("cid,h", [(6, 27), (5, 41), (8, 90)])
