@@ -74,18 +74,21 @@ def test_fullsize_sampled_rows(cid):
             what=f"config {cid} fused, 64 rows on every one of {cfg.heads} heads")
 
 
-def test_config2_all_rows_all_heads():
-    """Workload 2 (54,272 tokens x 8 heads, d128) in the launch configuration
-    the benchmark times for it (one fused call over all heads, the tail split
-    included), outputs NaN-poisoned, compared with the oracle on every row of
-    every head (1.2e13 fp64 FLOP on the host, one head per worker thread)."""
-    cfg = ti.config(2)
+@pytest.mark.parametrize("cid", [2, 3])
+def test_all_rows_all_heads(cid):
+    """Workload 2 (54,272 tokens x 8 heads, d128) and workload 3 (the isolated
+    microbenchmark shape, 107,126 tokens x 8 heads) in the launch
+    configuration the benchmark times for them (one fused call over all heads,
+    the tail split included), outputs NaN-poisoned, compared with the oracle on
+    every row of every head (1.2e13 and 4.7e13 fp64 FLOP on the host, spread
+    over threads)."""
+    cfg = ti.config(cid)
     lay = cfg.layout()
     q, k, v = ti.qkv(cfg)
     o, l = run_gpu(q, k, v, lay, cfg.params, poison=True)
-    log(f"config 2: N={lay.n} H={cfg.heads}; oracle on all rows and heads")
+    log(f"config {cid}: N={lay.n} H={cfg.heads}; oracle on all rows and heads")
     ro, rl = run_oracle_all_heads(q, k, v, lay, cfg.params)
-    compare(o.numpy(), l.numpy(), ro, rl, what=f"config 2, all {lay.n} rows of all {cfg.heads} heads")
+    compare(o.numpy(), l.numpy(), ro, rl, what=f"config {cid}, all {lay.n} rows of all {cfg.heads} heads")
 
 
 @pytest.mark.parametrize("cid,h", [(6, 27), (5, 41), (8, 90)])
