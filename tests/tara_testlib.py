@@ -108,43 +108,46 @@ def run_oracle(q, k, v, lay: ti.Layout, p: ti.Params, rows=None, heads: Optional
     return o, lse
 
 
-def run_oracle_all_heads(q, k, v, lay: ti.Layout, p: ti.Params, workers: int = 8, row_block: int = 32768):
-    """run_oracle on every row of every head of batch element 0, in jobs of one
-    head and up to row_block query rows on `workers` threads of this process
-    (NumPy releases the GIL inside its array loops; BLAS shares the host's
-    cores, at most 16, among them while they run). No child process is
-    started. Returns O [1, H, N, D], LSE [1, H, N]."""
+def run_oracle_all_heads(q, k, v, lay: ti.Layout, p: ti.Params, heads: Optional[Sequence[int]] = None,
+                         workers: int = 8, row_block: int = 32768):
+    """run_oracle on every row of the given heads (default all) of batch
+    element 0, in jobs of one head and up to row_block query rows on `workers`
+    threads of this process (NumPy releases the GIL inside its array loops;
+    BLAS shares the host's cores, at most 16, among them while they run). No
+    child process is started. Returns O [1, Hs, N, D], LSE [1, Hs, N]."""
     import os
     from concurrent.futures import ThreadPoolExecutor, as_completed
 
     from threadpoolctl import threadpool_limits
 
     _, H, N, D = q.shape
+    hs = list(range(H)) if heads is None else list(heads)
     workers = max(1, workers)
     blas_threads = max(1, min(16, len(os.sched_getaffinity(0))) // workers)
     pf = p.f32()
-    o = np.zeros((1, H, N, v.shape[-1]))
-    lse = np.zeros((1, H, N))
-    heads = {}
+    o = np.zeros((1, len(hs), N, v.shape[-1]))
+    lse = np.zeros((1, len(hs), N))
+    host = {}
 
     def head(h):
-        if h not in heads:
-            heads[h] = tuple(x[0, h].float().numpy() for x in (q, k, v))
-        return heads[h]
+        if h not in host:
+            host[h] = tuple(x[0, h].float().numpy() for x in (q, k, v))
+        return host[h]
 
     def job(h, r0, r1):
         qh, kh, vh = head(h)
         return h, r0, r1, oracle.attention_head(qh, kh, vh, lay.seg, lay.time, lay.picture, lay.mask, pf,
                                                 rows=np.arange(r0, r1))
 
-    for h in range(H):   # host copies made once, before the threads start
+    for h in hs:   # host copies made once, before the threads start
         head(h)
     with threadpool_limits(limits=blas_threads, user_api="blas"):
         with ThreadPoolExecutor(max_workers=workers) as ex:
-            futs = [ex.submit(job, h, r0, min(N, r0 + row_block)) for h in range(H) for r0 in range(0, N, row_block)]
+            futs = [ex.submit(job, h, r0, min(N, r0 + row_block)) for h in hs for r0 in range(0, N, row_block)]
             for fut in as_completed(futs):
                 h, r0, r1, (oh, lh) = fut.result()
-                o[0, h, r0:r1], lse[0, h, r0:r1] = oh, lh
+                i = hs.index(h)
+                o[0, i, r0:r1], lse[0, i, r0:r1] = oh, lh
                 log(f"oracle head {h}: rows {r0}..{r1 - 1} done")
     return o, lse
 

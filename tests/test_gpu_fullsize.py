@@ -103,13 +103,7 @@ def test_fullsize_all_rows_one_head(cid, h):
     lay = cfg.layout()
     q, k, v = ti.qkv(cfg)
     o, l = run_gpu(q, k, v, lay, cfg.params, heads=[h], poison=True)
-    blk = 8192
-    ro = np.zeros((1, 1, lay.n, cfg.head_dim))
-    rl = np.zeros((1, 1, lay.n))
-    for r0 in range(0, lay.n, blk):
-        rows = np.arange(r0, min(r0 + blk, lay.n))
-        ro[:, :, rows], rl[:, :, rows] = run_oracle(q, k, v, lay, cfg.params, rows=rows, heads=[h])
-        log(f"oracle head {h}: rows {r0}..{rows[-1]} done")
+    ro, rl = run_oracle_all_heads(q, k, v, lay, cfg.params, heads=[h], row_block=8192)
     compare(o.numpy(), l.numpy(), ro, rl, what=f"config {cid} head {h}, all {lay.n} rows")
 
 

@@ -16,3 +16,5 @@ def test_oracle_over_worker_processes_matches_in_process():
     o1, l1 = run_oracle(q, k, v, lay, p)
     o2, l2 = run_oracle_all_heads(q, k, v, lay, p, workers=3, row_block=37)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o3, l3 = run_oracle_all_heads(q, k, v, lay, p, heads=[2, 0], row_block=50)
+    assert np.array_equal(o3, o1[:, [2, 0]]) and np.array_equal(l3, l1[:, [2, 0]])
