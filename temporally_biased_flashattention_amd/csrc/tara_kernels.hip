@@ -21,7 +21,7 @@
 //                      tiles of its key range through LDS; its variants serve
 //                      key-range partitions, the three term passes, 8-bit Q.K
 //                      and the dense-bias baseline
-//   attn_f32_kernel    fp32 inputs: same arithmetic with FMA (correctness path)
+//   attn_f32_kernel    fp32 inputs: same arithmetic with FMA, K/V tiles staged in LDS
 //   merge_kernel       exact LSE merge of per-partition (O_p, LSE_p)
 //
 // Layout facts the bf16 kernel relies on (v_mfma_f32_32x32x16_bf16, wave64):
@@ -69,6 +69,14 @@ __device__ __forceinline__ float xor32_max(float x) {
 __device__ __forceinline__ float xor32_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the four lanes of a quad (lanes 4r .. 4r+3), by DPP quad permutes
+// (lane ^ 1, then lane ^ 2); every lane of the quad must be active.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  return x;
 }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
@@ -1458,15 +1466,26 @@ hipError_t launch_dense_bias(const AttnArgs& a, float* out, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------- fp32 path
-// Four lanes per query row, each holding D/4 dims of q and of the output;
-// keys are streamed from global memory (broadcast within the workgroup).
+// 64 query rows per workgroup, four lanes per row, each holding D/4 dims of q
+// and of the output. Key tiles of 64 keys (K and V rows, key times, picture
+// ids) are staged in LDS by the whole workgroup; each lane forms its row's
+// logits 16 keys at a time (partial dot products over its dims, summed across
+// the row's four lanes), rescales once per 16 keys to the new row max and adds
+// their weighted V rows to its output dims.
 constexpr int kF32Queries = 64;
+constexpr int kF32Keys = 64;
+constexpr int kF32Chunk = 16;
 
 template <int D, int PASS>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int DL = D / 4;
+  constexpr int KP = D + 4;   // LDS pitch of a staged row (floats): the four lanes' slices hit different banks
   constexpr bool PART = PASS != PASS_FUSED;
   constexpr bool TERM = PASS >= PASS_TERM_A;
+  __shared__ __attribute__((aligned(16))) float ks[kF32Keys * KP];
+  __shared__ __attribute__((aligned(16))) float vs[kF32Keys * KP];
+  __shared__ float tks[kF32Keys];
+  __shared__ int kps[kF32Keys];   // picture id (>= 0), -1 for other keys, -2 for keys outside this pass's range
   const int part = PASS == PASS_RANGE ? blockIdx.z : TERM ? PASS - PASS_TERM_A : 0;
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int N = a.N;
@@ -1475,8 +1494,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const bool qvalid = qrow < a.qr1;
   const int qr = qvalid ? qrow : a.qr1 - 1;
   const float* qp = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)qr * a.q_sn + sub * DL;
-  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh + sub * DL;
-  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh + sub * DL;
+  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh;
+  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh;
   float qv[DL], ov[DL];
 #pragma unroll
   for (int i = 0; i < DL; i += 4) {
@@ -1491,45 +1510,89 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int k0 = TERM ? 0 : a.kr[part], k1 = TERM ? N : a.kr[part + 1];
   const bool qb = tq == tq;
   float m = -INFINITY, l = 0.0f;
-  for (int kx = k0; kx < k1; ++kx) {
-    const float* kp = kg + (int64_t)kx * a.k_sn;
-    float sdot = 0.0f;
+  for (int kbase = k0 / kF32Keys * kF32Keys; kbase < k1; kbase += kF32Keys) {
+    __syncthreads();   // every lane is done with the previous tile
+    // stage the tile: rows of D floats as 16-byte chunks, zeros past [k0, k1)
 #pragma unroll
-    for (int i = 0; i < DL; i += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(kp + i);
-      sdot = fmaf(qv[i], x[0], sdot);
-      sdot = fmaf(qv[i + 1], x[1], sdot);
-      sdot = fmaf(qv[i + 2], x[2], sdot);
-      sdot = fmaf(qv[i + 3], x[3], sdot);
+    for (int it = 0; it < kF32Keys * D / 4 / 256; ++it) {
+      const int c = tid + it * 256;
+      const int r = c / (D / 4), col = (c % (D / 4)) * 4, key = kbase + r;
+      f32x4 kx = {}, vx = {};
+      if (key >= k0 && key < k1) {
+        kx = *reinterpret_cast<const f32x4*>(kg + (int64_t)key * a.k_sn + col);
+        vx = *reinterpret_cast<const f32x4*>(vg + (int64_t)key * a.v_sn + col);
+      }
+      *reinterpret_cast<f32x4*>(ks + r * KP + col) = kx;
+      *reinterpret_cast<f32x4*>(vs + r * KP + col) = vx;
     }
-    sdot += __shfl_xor(sdot, 1);
-    sdot += __shfl_xor(sdot, 2);
-    const float tk = tkb[kx];
-    const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);
-    const float pen = fminf(dd * dd, a.cap2);
-    const int pk = kpb[kx];
-    const float gain = pk >= 0 ? gtq[pk] : 0.0f;
-    const bool isg = tk == tk;   // a biased guide key
-    float x;
-    if (PASS == PASS_TERM_A) x = isg ? -INFINITY : fmaf(sdot, a.c, gain);
-    else if (PASS == PASS_TERM_B) x = isg ? fmaf(sdot, a.c, qb ? -a.cap2 : 0.0f) : -INFINITY;
-    else if (PASS == PASS_TERM_C) x = isg && qb ? fmaf(sdot, a.c, __log2f(1.0f - exp2f(pen - a.cap2)) - pen) : -INFINITY;
-    else x = fmaf(sdot, a.c, gain - pen);
-    if (x == -INFINITY) continue;   // the key is outside this pass (same for the row's 4 lanes)
-    const float mn = fmaxf(m, x);
-    const float alpha = exp2f(m - mn);
-    const float p = exp2f(x - mn);
-    l = fmaf(l, alpha, p);
-    const float* vp = vg + (int64_t)kx * a.v_sn;
+    if (tid < kF32Keys) {
+      const int key = kbase + tid;
+      const bool in = key >= k0 && key < k1;
+      tks[tid] = in ? tkb[key] : 0.0f;
+      kps[tid] = in ? kpb[key] : -2;
+    }
+    __syncthreads();
+    // chunks of kF32Chunk keys: the row's logits (log2 units; -inf: not a key
+    // of this pass), one rescale to the chunk's new row max (a row with no
+    // finite logit yet keeps m = -inf and exponent reference 0, so its
+    // weights stay 0), then the chunk's weighted V rows
+#pragma unroll 1
+    for (int j0 = 0; j0 < kF32Keys; j0 += kF32Chunk) {
+      float x[kF32Chunk];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < DL; i += 4) {
-      const f32x4 vv = *reinterpret_cast<const f32x4*>(vp + i);
-      ov[i] = fmaf(ov[i], alpha, p * vv[0]);
-      ov[i + 1] = fmaf(ov[i + 1], alpha, p * vv[1]);
-      ov[i + 2] = fmaf(ov[i + 2], alpha, p * vv[2]);
-      ov[i + 3] = fmaf(ov[i + 3], alpha, p * vv[3]);
+      for (int jj = 0; jj < kF32Chunk; ++jj) {
+        const int j = j0 + jj;
+        const float* kr = ks + j * KP + sub * DL;
+        float sdot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DL; i += 4) {
+          const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + i);
+          sdot = fmaf(qv[i], kx[0], sdot);
+          sdot = fmaf(qv[i + 1], kx[1], sdot);
+          sdot = fmaf(qv[i + 2], kx[2], sdot);
+          sdot = fmaf(qv[i + 3], kx[3], sdot);
+        }
+        sdot = quad_sum(sdot);   // the row's four lanes
+        const float tk = tks[j];
+        const int pk = kps[j];
+        const float dd = fmaxf(fmaf(fabsf(tq - tk), a.sigma, -a.w), 0.0f);
+        const float pen = fminf(dd * dd, a.cap2);
+        const float gain = pk >= 0 ? gtq[pk] : 0.0f;
+        const bool isg = tk == tk;   // a biased guide key
+        float xj;
+        if (PASS == PASS_TERM_A) xj = isg ? -INFINITY : fmaf(sdot, a.c, gain);
+        else if (PASS == PASS_TERM_B) xj = isg ? fmaf(sdot, a.c, qb ? -a.cap2 : 0.0f) : -INFINITY;
+        else if (PASS == PASS_TERM_C)
+          xj = isg && qb ? fmaf(sdot, a.c, __log2f(1.0f - exp2f(pen - a.cap2)) - pen) : -INFINITY;
+        else xj = fmaf(sdot, a.c, gain - pen);
+        if (pk == -2) xj = -INFINITY;
+        x[jj] = xj;
+        mt = fmaxf(mt, xj);
+      }
+      const float mn = fmaxf(m, mt);
+      const float mref = mn == -INFINITY ? 0.0f : mn;
+      const float alpha = exp2f(m - mref);
+      float ts = 0.0f;
+#pragma unroll
+      for (int i = 0; i < DL; ++i) ov[i] *= alpha;
+#pragma unroll
+      for (int jj = 0; jj < kF32Chunk; ++jj) {
+        const float p = exp2f(x[jj] - mref);
+        ts += p;
+        const float* vr = vs + (j0 + jj) * KP + sub * DL;
+#pragma unroll
+        for (int i = 0; i < DL; i += 4) {
+          const f32x4 vx = *reinterpret_cast<const f32x4*>(vr + i);
+          ov[i] = fmaf(p, vx[0], ov[i]);
+          ov[i + 1] = fmaf(p, vx[1], ov[i + 1]);
+          ov[i + 2] = fmaf(p, vx[2], ov[i + 2]);
+          ov[i + 3] = fmaf(p, vx[3], ov[i + 3]);
+        }
+      }
+      l = fmaf(l, alpha, ts);
+      m = mn;
     }
-    m = mn;
   }
   if (!qvalid) return;
   const bool empty = !(l > 0.0f);

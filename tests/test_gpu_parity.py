@@ -179,6 +179,30 @@ def test_fp32_d128_and_softmax_scale():
     check(q, k, v, lay, DEF, "bf16 scale 0.05", softmax_scale=0.05)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_tiles_ranges_and_terms(d):
+    """fp32 inputs over many 64-key tiles and a ragged last tile (2,937
+    tokens, 57 keys in the last tile), binding with a mask: the fused pass,
+    four key ranges with unaligned bounds (one of them a single key) and the
+    three term passes, every row of both heads against the oracle. Besides the
+    usual gates, fp32 arithmetic must land 10x inside them: the products and
+    sums are fp32 (unit roundoff 2^-24), so the logits carry errors near
+    D * 2^-24 |q||k| and O and LSE stay within 1e-3 and 1e-4 with a wide margin."""
+    lay = ti.make_layout(8, (10, 16), (10, 16), 2, 150, 77, mask=True)
+    n = lay.n
+    assert n == 2937 and n % 64 == 57
+    q, k, v = qkv_random(1, 2, n, d, seed=1500 + d, dtype=torch.float32)
+    p = ti.Params(window=0.10, falloff=0.40, strength=3.0, cap=8.0, binding=True, gains=(1.25, 0.75))
+    ro, rl = run_oracle(q, k, v, lay, p)
+    for what, kw in (("fused", {}),
+                     ("ranges", dict(mode="partitioned", partitions=4, bounds=[0, 700, 701, 2000, n])),
+                     ("three-term", dict(mode="three-term"))):
+        o, l = run_gpu(q, k, v, lay, p, poison=True, **kw)
+        compare(o.numpy(), l.numpy(), ro, rl, what=f"fp32 d={d} {what}")
+        compare(o.numpy(), l.numpy(), ro, rl, tol_o=1e-3, tol_lse=1e-4, tol_rel=1e-3,
+                what=f"fp32 d={d} {what}, fp32 gates")
+
+
 def test_segment_extremes():
     n = 700
     q, k, v = qkv_random(1, 2, n, 128, seed=15)
