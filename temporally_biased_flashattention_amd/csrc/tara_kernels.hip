@@ -269,7 +269,8 @@ hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, flo
 // so the tile's largest magnitude lands in [128, 256). Writes
 //   k8[b*H + h][n][d]  the scaled, rounded keys (rows past N are 0),
 //   ks[b*H + h][t]     the tile's scale,
-//   kmax[b*H + h][t]   max |k| over the tile's rows (bf16 values).
+//   kmax[b*H + h][t]   max |k| over the tile's rounded rows (E4M3 codes times
+//                      the scale), so that |q||k| bounds the 8-bit products.
 // 256 threads per tile: four adjacent threads per row, D/4 elements each.
 
 // floor(log2 |x|) of a finite x != 0 (exact, subnormals included)
@@ -285,6 +286,15 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// Sum of the squares of four E4M3 codes (the values pack_fp8x4 rounded to), in
+// fp32: the squares are exact, the sum rounds far inside the 2^-10 slack of the
+// attention kernel's norm bound.
+__device__ __forceinline__ float fp8x4_sumsq(uint32_t w) {
+  const float a = __builtin_amdgcn_cvt_f32_fp8((int)w, 0), b = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  const float c = __builtin_amdgcn_cvt_f32_fp8((int)w, 2), d = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  return fmaf(a, a, fmaf(b, b, fmaf(c, c, d * d)));
+}
+
 __global__ __launch_bounds__(256) void kquant_kernel(const __bf16* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
                                                      int H, int N, int D, int npad, int nkt, uint8_t* __restrict__ k8,
                                                      float* __restrict__ ks, float* __restrict__ kmax) {
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(256) void kquant_kernel(const __bf16* __restrict__ 
   const int dq = D / 4;
   const __bf16* kp = k + b * sb + h * sh + (int64_t)(valid ? n : 0) * sn + qd * dq;
   float v[32];
-  float ss = 0.0f, am = 0.0f;
+  float am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; i += 8) {
     if (i < dq) {
@@ -305,41 +315,40 @@ __global__ __launch_bounds__(256) void kquant_kernel(const __bf16* __restrict__ 
       for (int e = 0; e < 8; ++e) {
         const float f = valid ? (float)x[e] : 0.0f;
         v[i + e] = f;
-        ss = fmaf(f, f, ss);
         am = fmaxf(am, fabsf(f));
       }
     }
   }
-  ss += __shfl_xor(ss, 1);
-  ss += __shfl_xor(ss, 2);
-  float nm = sqrtf(ss);
-  for (int off = 32; off >= 1; off >>= 1) {
-    nm = fmaxf(nm, __shfl_xor(nm, off));
-    am = fmaxf(am, __shfl_xor(am, off));
-  }
-  if ((threadIdx.x & 63) == 0) {
-    wred[0][threadIdx.x >> 6] = nm;
-    wred[1][threadIdx.x >> 6] = am;
-  }
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if ((threadIdx.x & 63) == 0) wred[0][threadIdx.x >> 6] = am;
   __syncthreads();
-  nm = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
-  am = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
+  am = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
   const int e = am > 0.0f ? floor_log2(am) - 7 : 0;   // scale 2^e
   uint8_t* dst = k8 + ((int64_t)bh * npad + n) * D + qd * dq;
+  float ss = 0.0f;   // sum of squares of the row's E4M3 codes (this thread's share)
 #pragma unroll
   for (int i = 0; i < 32; i += 16) {
     if (i < dq) {
       u32x4 w;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
         w[j] = pack_fp8x4(ldexpf(v[i + 4 * j], -e), ldexpf(v[i + 4 * j + 1], -e), ldexpf(v[i + 4 * j + 2], -e),
                           ldexpf(v[i + 4 * j + 3], -e));
+        ss += fp8x4_sumsq(w[j]);
+      }
       *reinterpret_cast<u32x4*>(dst + i) = w;
     }
   }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  float nm = sqrtf(ss);   // the rounded row's norm over 2^e
+  for (int off = 32; off >= 1; off >>= 1) nm = fmaxf(nm, __shfl_xor(nm, off));
+  if ((threadIdx.x & 63) == 0) wred[1][threadIdx.x >> 6] = nm;
+  __syncthreads();
+  nm = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
   if (threadIdx.x == 0) {
     ks[(int64_t)bh * nkt + t] = ldexpf(1.0f, e);
-    kmax[(int64_t)bh * nkt + t] = nm;
+    kmax[(int64_t)bh * nkt + t] = ldexpf(nm, e);
   }
 }
 
@@ -797,7 +806,6 @@ void attn_bf16_kernel(AttnArgs a) {
           for (int e = 0; e < 8; ++e) {
             const float f = (float)x8[e];
             qv[st * 32 + u * 8 + e] = f;
-            q_ss = fmaf(f, f, q_ss);
             am = fmaxf(am, fabsf(f));
           }
         }
@@ -807,9 +815,11 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < D / 64; ++st)
 #pragma unroll
-        for (int w = 0; w < 8; ++w)
+        for (int w = 0; w < 8; ++w) {
           qf8[st][w] = (int)pack_fp8x4(ldexpf(qv[st * 32 + w * 4], -e), ldexpf(qv[st * 32 + w * 4 + 1], -e),
                                        ldexpf(qv[st * 32 + w * 4 + 2], -e), ldexpf(qv[st * 32 + w * 4 + 3], -e));
+          q_ss += fp8x4_sumsq((uint32_t)qf8[st][w]);   // |q|^2 of the rounded row over 2^(2e)
+        }
     }
   }
   const float tq = a.tq[(int64_t)b * N + qr];
@@ -959,9 +969,10 @@ void attn_bf16_kernel(AttnArgs a) {
   const __attribute__((address_space(4))) float* kscale_c =
       (const __attribute__((address_space(4))) float*)(Q8 ? a.ks + (int64_t)bh * a.nkt : a.kmax);
   const int krow_lane = perm32(lq);
-  // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum;
-  // with 8-bit Q.K also by (1 + 2^-4)^2 for the rounding of q and k to E4M3
-  const float qn_c = sqrtf(xor32_sum(q_ss)) * a.c * (Q8 ? 1.13f : 1.0f + 0x1.0p-10f);
+  // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum; with
+  // 8-bit Q.K, |q| and the key norms are those of the rounded values (E4M3
+  // codes times their scales), so the bound covers the 8-bit products as tightly
+  const float qn_c = sqrtf(xor32_sum(q_ss)) * (Q8 ? cq : a.c) * (1.0f + 0x1.0p-10f);
 
   f32x16 o[NDB];
 #pragma unroll
