@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline|2|3|4|5|7|8]
                     [--mode fused|partitioned|three-term|dense-bias|frame-loop] [--qk8]
+                    [--no-tile-skip]
 
 A step is one tara_attn_fwd call (metadata encoding, V layout pass, the fused
 attention kernel; in partitioned mode the range passes plus the merge; in
@@ -14,6 +15,9 @@ tokens, 107 latent frames) at 56 heads of dim 128 in bf16 with the default
 TARA controls. Prints one JSON line. --qk8 takes Q.K in FP8 E4M3 (per-row
 and per-key-tile power-of-two scales; P.V stays bf16); its roofline peak is
 that of the FLOP mix, half at the FP8 MFMA peak and half at the bf16 one.
+--no-tile-skip sends every key tile through the per-element bias (the
+library's TARA_DISABLE_TILE_SKIP switch), to measure what the tile classes
+buy; the results are the same up to rounding.
 
 Effective work per step is 4 * B * H * N^2 * D FLOP (both products over every
 query/key pair; bias skipping removes no contraction work).
@@ -238,6 +242,8 @@ def main():
                     choices=["fused", "partitioned", "three-term", "dense-bias", "frame-loop"])
     ap.add_argument("--partitions", type=int, default=3)
     ap.add_argument("--qk8", action="store_true", help="8-bit Q.K (bf16 workloads, fused mode)")
+    ap.add_argument("--no-tile-skip", action="store_true",
+                    help="every key tile takes the per-element bias (sets TARA_DISABLE_TILE_SKIP=1)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
@@ -254,6 +260,8 @@ def main():
               "TARA attention here is a single-GPU kernel and no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
 
+    if args.no_tile_skip:
+        os.environ["TARA_DISABLE_TILE_SKIP"] = "1"   # read by the library at every call
     import torch
 
     import tara_inputs as ti
@@ -337,7 +345,7 @@ def main():
     value = flop / (ms_step / 1e3) / 1e12
     k_avg = sum(kms) / len(kms) if kms else float("nan")
     achieved = flop / (k_avg / 1e3) / 1e12
-    traffic = None if args.qk8 else measured_traffic(f"{cfg.name} {args.mode}")
+    traffic = None if args.qk8 or args.no_tile_skip else measured_traffic(f"{cfg.name} {args.mode}")
     # fp32 inputs run the FMA path: bound by the fp32 vector ALUs, not the MFMA units
     fp32_path = cfg.dtype != "bf16"
     peak = PEAK_FP32_VALU_TFLOPS if fp32_path else PEAK_QK8_TFLOPS if args.qk8 else PEAK_BF16_TFLOPS
@@ -359,9 +367,12 @@ def main():
         "step_ms": {"mean": round(ms_step, 3), "median": round(step_ms[len(step_ms) // 2], 3),
                     "min": round(step_ms[0], 3), "max": round(step_ms[-1], 3)},
         "gfx_clock_mhz": clock.summary(),
-        "config": {"workload": f"{cfg.name} ({args.mode}{', 8-bit Q.K' if args.qk8 else ''})", "tokens": N, "heads": H, "head_dim": D, "batch": B,
+        "config": {"workload": f"{cfg.name} ({args.mode}{', 8-bit Q.K' if args.qk8 else ''}"
+                               f"{', per-element bias on every tile' if args.no_tile_skip else ''})", "tokens": N, "heads": H, "head_dim": D, "batch": B,
                    "target_tokens": int((lay.seg == 0).sum()), "guide_tokens": int((lay.seg == 1).sum()),
                    "mode": args.mode, "partitions": info.get("num_partitions"), "qk8": args.qk8,
+                   # false: every key tile took the per-element bias (--no-tile-skip)
+                   "tile_skip": not info.get("elem_all"),
                    "controls": {"window": cfg.params.window, "falloff": cfg.params.falloff,
                                 "strength": cfg.params.strength, "cap": cfg.params.cap,
                                 "binding": cfg.params.binding, "gains": list(cfg.params.gains),
