@@ -506,7 +506,8 @@ int enqueue_call(const Call& c, char* ws, bool run_meta, bool debug, hipStream_t
                                 const_cast<__bf16*>(aa.vt), B, H, N, npad, D, stream);
     ++launches;
     if (e == hipSuccess) {
-      // key norms per tile; with 8-bit Q.K the same kernel also writes the FP8 keys and tile scales
+      // max key norm per tile; with 8-bit Q.K the quantising kernel instead, which writes the FP8
+      // keys, the tile scales and the norms of the rounded keys
       if (qk8)
         e = launch_kquant(static_cast<const __bf16*>(k), k_str[0], k_str[1], k_str[2],
                                 const_cast<uint8_t*>(aa.k8), const_cast<float*>(aa.ks), const_cast<float*>(aa.kmax),
