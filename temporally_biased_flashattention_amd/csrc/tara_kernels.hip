@@ -37,6 +37,7 @@
 // V^T fragments are single 16-byte LDS reads.
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -253,7 +254,9 @@ __global__ __launch_bounds__(256) void knorm_kernel(const __bf16* __restrict__ k
   if (lane == 0) wmax[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0)
-    kmax[(int64_t)bh * nkt + t] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    // a norm past the fp32 range is held at FLT_MAX, so that the attention
+    // kernel's bound |q| max|k| never becomes 0 * inf
+    kmax[(int64_t)bh * nkt + t] = fminf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])), FLT_MAX);
 }
 
 hipError_t launch_knorm(const __bf16* k, int64_t sb, int64_t sh, int64_t sn, float* kmax, int B, int H, int N,
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(256) void kquant_kernel(const __bf16* __restrict__ 
   nm = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
   if (threadIdx.x == 0) {
     ks[(int64_t)bh * nkt + t] = ldexpf(1.0f, e);
-    kmax[(int64_t)bh * nkt + t] = ldexpf(nm, e);
+    kmax[(int64_t)bh * nkt + t] = fminf(ldexpf(nm, e), FLT_MAX);   // as in knorm_kernel
   }
 }
 
@@ -972,7 +975,9 @@ void attn_bf16_kernel(AttnArgs a) {
   // |q| * c, rounded up by 2^-10 to cover fp32 rounding of the MFMA sum; with
   // 8-bit Q.K, |q| and the key norms are those of the rounded values (E4M3
   // codes times their scales), so the bound covers the 8-bit products as tightly
-  const float qn_c = sqrtf(xor32_sum(q_ss)) * (Q8 ? cq : a.c) * (1.0f + 0x1.0p-10f);
+  // (held at FLT_MAX like the key norms: the bound of a zero row against a
+  // zero tile stays 0, the exact maximum, instead of 0 * inf)
+  const float qn_c = fminf(sqrtf(xor32_sum(q_ss)) * (Q8 ? cq : a.c) * (1.0f + 0x1.0p-10f), FLT_MAX);
 
   f32x16 o[NDB];
 #pragma unroll
