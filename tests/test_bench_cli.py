@@ -35,6 +35,17 @@ def test_needs_a_gpu_here():
     assert r.returncode == 2 and "needs a GPU" in r.stderr
 
 
+def test_tile_skip_switch_accepted():
+    """--no-tile-skip (the A/B of the tile classes) is a known option: without
+    a GPU the run stops at the GPU check, not at the argument parser."""
+    import torch
+    if torch.cuda.is_available():
+        import pytest
+        pytest.skip("a GPU is present")
+    r = _run("--no-tile-skip", "--steps", "1", "--warmup", "0")
+    assert r.returncode == 2 and "needs a GPU" in r.stderr and "unrecognized" not in r.stderr
+
+
 def test_attention_flop_hand_count():
     """The metric's FLOP count against a count done by hand. One head, 2 query
     rows, 3 keys, head dim 4: Q.K^T is 2 x 3 dot products of length 4, each 4
